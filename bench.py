@@ -1,0 +1,302 @@
+"""Benchmark of the WISE working-set attention path on one MI355X.
+
+One bench "step" is one full T = 32 recurrent-step attention trajectory of the
+WISE method on the synthetic workload (default: 4k -- bf16, batch 1, 32 heads,
+head_dim 128, n = 4096, block 32, eta = 0.95):
+  steps 1..8    dense causal attention                      (wise_dense_attn)
+  steps 9..12   dense attention + block-mass epilogue        (wise_full_attn_mass)
+  once          selection + temporal union + CSR             (wise_build_support)
+  steps 13..32  block-sparse attention over the schedule     (wise_sparse_attn)
+The in-run baseline -- 32 dense steps on the same inputs -- is timed in the same
+passes, alternating which of the two runs first.  Every step reads its own
+pre-generated Q/K/V, resident in HBM before timing starts.
+
+Printed JSON line: value = late-step sparse effective TFLOP/s (4*d FLOP per
+scheduled admissible (query, key) pair, kernel-only), ms_per_step = WISE 32-step
+attention ms, plus setup-inclusive / kernel-only late-step speedups over the
+in-house dense kernel, the dense trajectory, the roofline of the sparse kernel
+and the fp64 CPU oracle timed on a bounded sample (the cpu_baseline leg).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+METRIC = "late-step sparse attn TFLOP/s + speedup vs dense at 4K; 32-step attn ms"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+DISCOVERY_DENSE = range(1, 9)
+DISCOVERY_MASS = range(9, 13)
+REUSE = range(13, 33)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pairs_from_csr(row_ptr, col_idx, nq):
+    """Scheduled admissible (query, key) pairs of a CSR schedule (host arrays)."""
+    total = 0
+    for r in range(len(row_ptr) - 1):
+        qb = r % nq
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        off = int(np.count_nonzero((cols >= 0) & (cols < qb)))
+        diag = int(np.count_nonzero(cols == qb))
+        total += off * 32 * 32 + diag * 32 * 33 // 2
+    return total
+
+
+def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
+    """The fp64 oracle on a bounded sample: heads 0.. of the same workload, timed
+    per stage; the late-step rate is scheduled-pair FLOP / oracle sparse time."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    heads_done = 0
+    t_sparse = t_dense = t_mass = t_sel = 0.0
+    flops = 0
+    start = time.perf_counter()
+    for h in range(w.heads):
+        qkv = {t: gen_f32(t, h) for t in (1, 9, 10, 11, 12, 13)}
+        t0 = time.perf_counter()
+        O.causal_attention(*qkv[1])
+        t1 = time.perf_counter()
+        masses = [O.block_mass(qkv[t][0], qkv[t][1]) for t in (9, 10, 11, 12)]
+        t2 = time.perf_counter()
+        sup = O.union_supports([O.step_supports(m, eta) for m in masses])
+        t3 = time.perf_counter()
+        O.sparse_attention(*qkv[13], sup)
+        t4 = time.perf_counter()
+        t_dense += t1 - t0
+        t_mass += (t2 - t1) / 4 + (t1 - t0)   # mass step = attention + block mass
+        t_sel += t3 - t2
+        t_sparse += t4 - t3
+        flops += 4 * w.head_dim * O.scheduled_pairs(sup, w.nq)
+        heads_done += 1
+        if time.perf_counter() - start > budget_s:
+            break
+    scale = w.heads / heads_done
+    traj_s = scale * (8 * t_dense + 4 * t_mass + t_sel + 20 * t_sparse)
+    return {
+        "value": flops / t_sparse / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle on heads 0..{heads_done - 1} of {w.heads} of the {w.name} workload: "
+                   f"one dense step, four block-mass steps, selection+union, one sparse step (step 13); "
+                   f"value = late-step scheduled-pair FLOP / oracle sparse time"),
+        "sparse_step_ms_extrapolated": 1e3 * scale * t_sparse,
+        "trajectory_ms_extrapolated": 1e3 * traj_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10, help="timed trajectories (balanced passes)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="4k")
+    ap.add_argument("--eta", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_wise_amd import wise
+    from block_sparse_attention_wise_amd.synthetic import WORKLOADS, Generator
+
+    w = WORKLOADS[args.workload]
+    eta = args.eta if args.eta is not None else w.etas[0]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] generating {w.name} inputs for 32 steps")
+    t0 = time.time()
+    gen = Generator(w)
+    steps = {}
+    for t in range(1, 33):
+        steps[t] = tuple(x.to(dev) for x in gen.step_torch(t))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f}s)")
+
+    bh, nq = w.batch * w.heads, w.nq
+    out = torch.empty_like(steps[1][0])
+    mass = torch.empty((4, bh, nq, nq), dtype=torch.float32, device=dev)
+    sched = wise.alloc_schedule(bh, nq, dev)
+    ws = torch.empty(wise.build_support_workspace_bytes(bh, nq, 4), dtype=torch.uint8, device=dev)
+    full_sched = wise.alloc_schedule(bh, nq, dev)
+    wise.build_support(torch.ones((1, bh, nq, nq), dtype=torch.float32, device=dev), 1.0,
+                       schedule=full_sched, workspace=ws)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def wise_traj():
+        e = [ev() for _ in range(5)]
+        e[0].record(stream)
+        for t in DISCOVERY_DENSE:
+            wise.dense_attn(*steps[t], out=out)
+        e[1].record(stream)
+        for si, t in enumerate(DISCOVERY_MASS):
+            wise.full_attn_mass(*steps[t], out=out, mass=mass[si])
+        e[2].record(stream)
+        wise.build_support(mass, eta, schedule=sched, workspace=ws)
+        e[3].record(stream)
+        for t in REUSE:
+            wise.sparse_attn(*steps[t], sched, out=out)
+        e[4].record(stream)
+        return e
+
+    def dense_traj():
+        e = [ev() for _ in range(3)]
+        e[0].record(stream)
+        for t in range(1, 13):
+            wise.dense_attn(*steps[t], out=out)
+        e[1].record(stream)
+        for t in REUSE:
+            wise.dense_attn(*steps[t], out=out)
+        e[2].record(stream)
+        return e
+
+    def matched_full():
+        e = [ev() for _ in range(2)]
+        e[0].record(stream)
+        for t in REUSE:
+            wise.sparse_attn(*steps[t], full_sched, out=out)
+        e[1].record(stream)
+        return e
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        wise_traj()
+        dense_traj()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} balanced passes")
+    recs = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for p in range(args.steps):
+        if p % 2 == 0:
+            a = wise_traj()
+            b = dense_traj()
+        else:
+            b = dense_traj()
+            a = wise_traj()
+        recs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    m_rec = [matched_full() for _ in range(max(3, args.steps // 2))]
+    torch.cuda.synchronize()
+
+    def ms(e0, e1):
+        return e0.elapsed_time(e1)
+
+    ph = {k: [] for k in ("disc_dense", "disc_mass", "build", "reuse", "wise_traj", "dense_early", "dense_late",
+                          "dense_traj")}
+    for a, b in recs:
+        ph["disc_dense"].append(ms(a[0], a[1]))
+        ph["disc_mass"].append(ms(a[1], a[2]))
+        ph["build"].append(ms(a[2], a[3]))
+        ph["reuse"].append(ms(a[3], a[4]))
+        ph["wise_traj"].append(ms(a[0], a[4]))
+        ph["dense_early"].append(ms(b[0], b[1]))
+        ph["dense_late"].append(ms(b[1], b[2]))
+        ph["dense_traj"].append(ms(b[0], b[2]))
+    med = {k: statistics.median(v) for k, v in ph.items()}
+    iqr = {k: float(np.percentile(v, 75) - np.percentile(v, 25)) for k, v in ph.items()}
+    matched_ms = statistics.median(ms(e[0], e[1]) for e in m_rec)
+
+    rp = sched.row_ptr.cpu().numpy().astype(np.int64)
+    ci = sched.col_idx.cpu().numpy().astype(np.int64)
+    pairs = pairs_from_csr(rp, ci, nq)
+    nnz = int(rp[-1])
+    causal_blocks = bh * nq * (nq + 1) // 2
+    sparse_flop = 4.0 * w.head_dim * pairs                 # per sparse launch
+    dense_pairs = bh * (w.seqlen * (w.seqlen + 1) // 2)
+    dense_flop = 4.0 * w.head_dim * dense_pairs
+    sparse_ms = med["reuse"] / len(REUSE)                  # average launch duration
+    dense_ms = med["dense_late"] / len(REUSE)
+    tflops = sparse_flop / (sparse_ms * 1e-3) / 1e12
+    dense_tflops = dense_flop / (dense_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med["wise_traj"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "seq_len": w.seqlen, "block": 32, "eta": eta, "recurrent_steps": 32,
+                   "discovery_union_steps": [9, 12], "reuse_steps": [13, 32]},
+        "late_step_tflops": round(tflops, 3),
+        "late_step_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "late_step_tflops_setup_inclusive": round(len(REUSE) * sparse_flop / ((med["reuse"] + med["build"]) * 1e-3)
+                                                  / 1e12, 3),
+        "dense_kernel_tflops": round(dense_tflops, 3),
+        "dense_kernel_frac_of_peak": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
+        "late_speedup_kernel_only": round(med["dense_late"] / med["reuse"], 4),
+        "late_speedup_setup_inclusive": round(med["dense_late"] / (med["reuse"] + med["build"]), 4),
+        "matched_full_support_late_ms": round(matched_ms, 4),
+        "matched_speedup": round(matched_ms / med["reuse"], 4),
+        "wise_trajectory_ms": round(med["wise_traj"], 4),
+        "dense_trajectory_ms": round(med["dense_traj"], 4),
+        "trajectory_speedup": round(med["dense_traj"] / med["wise_traj"], 4),
+        "phase_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "phase_ms_iqr": {k: round(v, 4) for k, v in iqr.items()},
+        "block_density": round(nnz / causal_blocks, 5),
+        "pair_density": round(pairs / dense_pairs, 5),
+        "nnz_blocks": nnz,
+        "timed_wall_s": round(wall, 3),
+        "roofline": {
+            "kernel": "wise_sparse_attn (attn_bf16_kernel<128,sparse>)",
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flop_per_launch": sparse_flop,
+            "avg_launch_ms": round(sparse_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+
+        per_head = {}
+
+        def gen_f32(t, h):
+            # regenerated on the host for one head: the same cast values the GPU read
+            if h not in per_head:
+                per_head[h] = Generator(w, heads=[h])
+            return tuple(x[0, 0].to(torch.float64).numpy() for x in per_head[h].step_torch(t))
+
+        result["cpu_baseline"] = cpu_baseline(w, eta, gen_f32, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

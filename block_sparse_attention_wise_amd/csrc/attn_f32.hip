@@ -1,0 +1,156 @@
+// fp32 causal attention kernels (dense with optional block mass, and block-sparse)
+// for gfx950: fp32 inputs, fp32 arithmetic on the vector ALUs.  Used for
+// fp32 workloads where the bf16 MFMA path's rounding is not acceptable.
+//
+// The WISE paper (Wan & Chen, arXiv 2609.27373): attention of §3, block mass of
+// §5.1 (Eq. 5), reuse mask of §5.2, CSR schedule of App. B.
+//
+// One 256-thread workgroup owns one (batch*head, query block) row of 32 queries.
+// Q, K and V tiles are staged in LDS; thread t computes scores of query t/8
+// against keys 4*(t%8) .. +3, and output columns t%8 + 8*u of query t/8.
+#include "common.h"
+#include "kernels.h"
+
+namespace wise {
+
+// max / sum over the 8 consecutive lanes that share one query row
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  return fmaxf(x, __shfl_xor(x, 4));
+}
+__device__ __forceinline__ float group8_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x + __shfl_xor(x, 4);
+}
+
+template <int D, bool SPARSE, bool MASS>
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
+  constexpr int S = D + 1;  // padded LDS stride (floats)
+  constexpr int NU = D / 8;
+  __shared__ float qs[32 * S];
+  __shared__ float ks[32 * S];
+  __shared__ float vs[32 * S];
+  __shared__ float ps[32 * 33];
+  __shared__ float red[8];
+
+  const int tid = threadIdx.x;
+  const int qi = tid >> 3, sub = tid & 7;
+  const int logical = xcd_remap(blockIdx.x, a.rows);
+  const int bh = logical / a.nq;
+  const int qb = a.nq - 1 - (logical - bh * a.nq);
+  const int row = bh * a.nq + qb;
+  const size_t head_off = (size_t)bh * a.seqlen * D;
+  const float* qh = a.q + head_off + (size_t)(32 * qb) * D;
+
+  for (int e = tid; e < 32 * D; e += 256) qs[(e / D) * S + e % D] = qh[e];
+
+  int beg = 0, end = qb + 1;
+  if (SPARSE) {
+    int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
+    b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
+    b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
+    beg = (int)b0;
+    end = (int)b1;
+  }
+
+  float acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int qrow = 32 * qb + qi;
+
+  for (int it = beg; it < end; ++it) {
+    const int b = SPARSE ? a.col_idx[it] : it;
+    if (SPARSE && (b < 0 || b > qb)) continue;
+    __syncthreads();
+    const float* kb = a.k + head_off + (size_t)(32 * b) * D;
+    const float* vb = a.v + head_off + (size_t)(32 * b) * D;
+    for (int e = tid; e < 32 * D; e += 256) {
+      ks[(e / D) * S + e % D] = kb[e];
+      vs[(e / D) * S + e % D] = vb[e];
+    }
+    __syncthreads();
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 4 * sub + c;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(qs[qi * S + d], ks[j * S + d], dot);
+      float x = dot * a.scale;
+      if (32 * b + j > qrow) x = -INFINITY;
+      sc[c] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = group8_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = expf(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float p = expf(sc[c] - m_new);
+      ps[qi * 33 + 4 * sub + c] = p;
+      psum += p;
+    }
+    l_run = l_run * alpha + group8_sum(psum);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int d = sub + 8 * u;
+      float x = acc[u] * alpha;
+      for (int j = 0; j < 32; ++j) x = fmaf(ps[qi * 33 + j], vs[j * S + d], x);
+      acc[u] = x;
+    }
+  }
+
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  float* orow = a.o + head_off + (size_t)qrow * D;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) orow[sub + 8 * u] = acc[u] * inv;
+  const float lse = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+  if (a.lse != nullptr && sub == 0) a.lse[(size_t)bh * a.seqlen + qrow] = lse;
+
+  if (MASS) {
+    float* mrow = a.mass + (size_t)row * a.nq;
+    for (int b = 0; b <= qb; ++b) {
+      __syncthreads();
+      const float* kb = a.k + head_off + (size_t)(32 * b) * D;
+      for (int e = tid; e < 32 * D; e += 256) ks[(e / D) * S + e % D] = kb[e];
+      __syncthreads();
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * sub + c;
+        if (32 * b + j > qrow) continue;
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(qs[qi * S + d], ks[j * S + d], dot);
+        part += expf(dot * a.scale - lse);
+      }
+      part = wave_sum(part);
+      if ((tid & 63) == 0) red[tid >> 6] = part;
+      __syncthreads();
+      if (tid == 0) mrow[b] = (red[0] + red[1] + red[2] + red[3]) * (1.f / 32.f);
+    }
+    for (int b = qb + 1 + tid; b < a.nq; b += 256) mrow[b] = 0.f;
+  }
+}
+
+template <int D, bool SPARSE, bool MASS>
+static hipError_t launch(const AttnF32Args& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_f32_kernel<D, SPARSE, MASS>), dim3(a.rows), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream) {
+  if (head_dim == 128) {
+    if (sparse) return launch<128, true, false>(a, stream);
+    return mass ? launch<128, false, true>(a, stream) : launch<128, false, false>(a, stream);
+  }
+  if (sparse) return launch<64, true, false>(a, stream);
+  return mass ? launch<64, false, true>(a, stream) : launch<64, false, false>(a, stream);
+}
+
+}  // namespace wise

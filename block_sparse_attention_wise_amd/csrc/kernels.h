@@ -1,0 +1,48 @@
+// Launch interfaces between the C ABI shim and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wise {
+
+struct AttnBf16Args {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;                // nullable
+  float* mass;               // nullable; dense kernel only
+  const int32_t* row_ptr;    // sparse kernel only
+  const int32_t* col_idx;    // sparse kernel only
+  int64_t col_cap;           // readable col_idx entries (<= INT32_MAX)
+  int seqlen;
+  int nq;
+  int rows;                  // batch * heads * nq
+  float scale_log2;          // softmax scale * log2(e)
+};
+
+struct AttnF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  float* mass;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t col_cap;
+  int seqlen;
+  int nq;
+  int rows;
+  float scale;               // softmax scale (natural-log units)
+};
+
+hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
+size_t support_workspace_bytes(int bh, int nq);
+hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int32_t* row_ptr,
+                          int32_t* col_idx, int32_t* nnz, void* workspace, hipStream_t stream);
+
+}  // namespace wise

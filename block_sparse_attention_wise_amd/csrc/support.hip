@@ -1,0 +1,217 @@
+// Working-set schedule construction for gfx950: per-step cumulative-eta block
+// selection, temporal union and CSR compaction.
+//
+// The WISE paper (Wan & Chen, arXiv 2609.27373): the cumulative-eta support of
+// §3 applied to the block masses of §5.1, the temporal union of App. B (WISE
+// configuration) and the CSR schedule of App. B (sparse-kernel implementation).
+//
+// Three kernels:
+//   select_union  one 256-thread workgroup per (batch*head, query block) row.
+//                 For every step: the q+1 admissible masses are bitonic-sorted in
+//                 LDS by the 64-bit key (mass desc, index asc); an exclusive fp64
+//                 prefix sum over the sorted masses marks block k as selected iff
+//                 the mass before it is still below eta; selected blocks are ORed
+//                 into the row's union bitmask.  Writes the bitmask and its
+//                 popcount to the workspace.
+//   scan_counts   one workgroup: exclusive scan of the per-row counts -> row_ptr,
+//                 nnz.
+//   emit_csr      one wavefront per row: expands the bitmask into ascending
+//                 col_idx entries at row_ptr[row].
+#include "common.h"
+#include "kernels.h"
+
+namespace wise {
+
+constexpr int kSelThreads = 256;
+constexpr int kMaxNq = 4096;
+
+// Order-preserving map of an fp32 bit pattern to uint32 (larger float -> larger uint).
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+struct SupportArgs {
+  const float* mass;  // [steps][rows][nq][nq] with rows here = bh
+  int bh, nq, steps;
+  double eta;
+  uint32_t* masks;    // [bh*nq][nwords]
+  int32_t* counts;    // [bh*nq]
+  int nwords;
+};
+
+__device__ __forceinline__ double block_exclusive_scan(double x, double* wsum, int tid) {
+  // inclusive scan within the wavefront
+  const int lane = tid & 63, w = tid >> 6;
+  double inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int k = 0; k < w; ++k) base += wsum[k];
+  __syncthreads();
+  return base + inc - x;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a) {
+  __shared__ uint64_t keys[kMaxNq];
+  __shared__ uint32_t uni[kMaxNq / 32];
+  __shared__ double wsum[kSelThreads / 64];
+  __shared__ int cnt_part[kSelThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int qb = row % a.nq;
+  const int bh = row / a.nq;
+  const int n = qb + 1;
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+
+  for (int w = tid; w < a.nwords; w += kSelThreads) uni[w] = 0u;
+
+  for (int t = 0; t < a.steps; ++t) {
+    const float* mrow = a.mass + (((size_t)t * a.bh + bh) * a.nq + qb) * (size_t)a.nq;
+    __syncthreads();
+    for (int e = tid; e < n2; e += kSelThreads)
+      keys[e] = e < n ? ((uint64_t)ordered_bits(mrow[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+    __syncthreads();
+    // bitonic sort, descending
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int e = tid; e < (n2 >> 1); e += kSelThreads) {
+          const int lo = 2 * e - (e & (stride - 1));
+          const int hi = lo + stride;
+          const bool desc = (lo & size) == 0;
+          const uint64_t x = keys[lo], y = keys[hi];
+          if ((x < y) == desc) {
+            keys[lo] = y;
+            keys[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // exclusive fp64 prefix over the sorted masses; each thread owns a contiguous chunk
+    const int per = (n + kSelThreads - 1) / kSelThreads;
+    const int c0 = tid * per;
+    const int c1 = min(n, c0 + per);
+    double local = 0.0;
+    for (int e = c0; e < c1; ++e) local += (double)from_ordered_bits((uint32_t)(keys[e] >> 32));
+    double run = block_exclusive_scan(local, wsum, tid);
+    for (int e = c0; e < c1; ++e) {
+      const uint64_t key = keys[e];
+      if (a.eta >= 1.0 || run < a.eta) {
+        const uint32_t b = 0xffffffffu - (uint32_t)(key & 0xffffffffu);
+        atomicOr(&uni[b >> 5], 1u << (b & 31));
+      }
+      run += (double)from_ordered_bits((uint32_t)(key >> 32));
+    }
+  }
+  __syncthreads();
+  int c = 0;
+  uint32_t* out = a.masks + (size_t)row * a.nwords;
+  for (int w = tid; w < a.nwords; w += kSelThreads) {
+    out[w] = uni[w];
+    c += __popc(uni[w]);
+  }
+  // block sum of c
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if ((tid & 63) == 0) cnt_part[tid >> 6] = c;
+  __syncthreads();
+  if (tid == 0) a.counts[row] = cnt_part[0] + cnt_part[1] + cnt_part[2] + cnt_part[3];
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_counts_kernel(const int32_t* counts, int rows,
+                                                                    int32_t* row_ptr, int32_t* nnz) {
+  __shared__ int32_t wtot[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (rows + kScanThreads - 1) / kScanThreads;
+  const int c0 = tid * per, c1 = min(rows, c0 + per);
+  int local = 0;
+  for (int e = c0; e < c1; ++e) local += counts[e];
+  int inc = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wtot[w] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int k = 0; k < w; ++k) base += wtot[k];
+  int run = base + inc - local;
+  for (int e = c0; e < c1; ++e) {
+    row_ptr[e] = run;
+    run += counts[e];
+  }
+  if (tid == kScanThreads - 1) {
+    row_ptr[rows] = run;
+    *nnz = run;
+  }
+}
+
+__global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int nwords, const int32_t* row_ptr,
+                                                       int32_t* col_idx) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const uint32_t* m = masks + (size_t)row * nwords;
+  int base = row_ptr[row];
+  for (int w0 = 0; w0 < nwords; w0 += 64) {
+    const int w = w0 + lane;
+    const uint32_t bits = w < nwords ? m[w] : 0u;
+    const int c = __popc(bits);
+    int inc = c;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    int pos = base + inc - c;
+    uint32_t rem = bits;
+    while (rem) {
+      const int bit = __ffs(rem) - 1;
+      col_idx[pos++] = 32 * w + bit;
+      rem &= rem - 1;
+    }
+    base += __shfl(inc, 63);
+  }
+}
+
+size_t support_workspace_bytes(int bh, int nq) {
+  const size_t rows = (size_t)bh * nq;
+  const size_t nwords = (nq + 31) / 32;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(rows * nwords * 4) + al(rows * 4);
+}
+
+hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int32_t* row_ptr,
+                          int32_t* col_idx, int32_t* nnz, void* workspace, hipStream_t stream) {
+  const size_t rows = (size_t)bh * nq;
+  const int nwords = (nq + 31) / 32;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  SupportArgs a;
+  a.mass = mass;
+  a.bh = bh;
+  a.nq = nq;
+  a.steps = steps;
+  a.eta = eta;
+  a.masks = static_cast<uint32_t*>(workspace);
+  a.counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4));
+  a.nwords = nwords;
+  hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, a.counts, (int)rows, row_ptr, nnz);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.masks, nwords, row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+}  // namespace wise

@@ -1,0 +1,129 @@
+// Host side of the C ABI declared in include/wise.h: argument validation (pure
+// host code, no HIP call before it passes), launch selection and status codes.
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "wise.h"
+
+namespace wise {
+namespace {
+
+constexpr int kBlock = 32;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shape checks shared by the attention entry points.  Returns WISE_OK or the error.
+wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
+                             const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             float scale) {
+  if (dt != WISE_BF16 && dt != WISE_FP32) return WISE_ERR_INVALID_ARG;
+  if (batch <= 0 || heads <= 0 || seqlen <= 0 || head_dim <= 0 || block <= 0) return WISE_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o) return WISE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WISE_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return WISE_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return WISE_ERR_INVALID_ARG;
+  if (block != kBlock) return WISE_ERR_UNSUPPORTED;
+  if (seqlen % block != 0) return WISE_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return WISE_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)batch * heads * (seqlen / block);
+  const int64_t elems = (int64_t)batch * heads * seqlen * head_dim;
+  if (rows > INT32_MAX || elems > ((int64_t)1 << 40)) return WISE_ERR_INVALID_ARG;
+  return WISE_OK;
+}
+
+float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim); }
+
+wise_status run_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, const void* q, const void* k,
+                     const void* v, void* o, float* lse, float* mass, const int32_t* row_ptr,
+                     const int32_t* col_idx, int64_t col_cap, bool sparse, float scale, void* stream) {
+  if (col_cap > INT32_MAX) col_cap = INT32_MAX;
+  const int nq = seqlen / kBlock;
+  const int rows = batch * heads * nq;
+  const float sc = resolve_scale(scale, head_dim);
+  hipError_t e;
+  if (dt == WISE_BF16) {
+    AttnBf16Args a{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                   static_cast<__bf16*>(o), lse, mass, row_ptr, col_idx, col_cap, seqlen, nq, rows,
+                   sc * 1.4426950408889634f};
+    e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
+  } else {
+    AttnF32Args a{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                  static_cast<float*>(o), lse, mass, row_ptr, col_idx, col_cap, seqlen, nq, rows, sc};
+    e = launch_attn_f32(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
+  }
+  return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace wise
+
+using namespace wise;
+
+extern "C" {
+
+int wise_abi_version(void) { return WISE_ABI_VERSION; }
+
+const char* wise_status_string(wise_status s) {
+  switch (s) {
+    case WISE_OK: return "ok";
+    case WISE_ERR_INVALID_ARG: return "invalid argument";
+    case WISE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case WISE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
+                                const void* q, const void* k, const void* v, void* o, float* lse, float* mass,
+                                float scale, void* stream) {
+  wise_status st = check_attn_shape(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
+  if (st != WISE_OK) return st;
+  if (mass && !aligned4(mass)) return WISE_ERR_INVALID_ARG;
+  return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, mass, nullptr, nullptr, 0, false, scale,
+                  stream);
+}
+
+wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
+                            const void* q, const void* k, const void* v, void* o, float* lse, float scale,
+                            void* stream) {
+  return wise_full_attn_mass(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, scale, stream);
+}
+
+size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps) {
+  if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return 0;
+  if ((int64_t)bh * nq > INT32_MAX) return 0;
+  return support_workspace_bytes(bh, nq);
+}
+
+wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta, int32_t* row_ptr,
+                               int32_t* col_idx, int64_t col_capacity, int32_t* nnz, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
+  if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
+  if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
+    return WISE_ERR_INVALID_ARG;
+  if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
+  const int64_t worst = (int64_t)bh * nq * (nq + 1) / 2;
+  if (worst > INT32_MAX) return WISE_ERR_INVALID_ARG;
+  if (col_capacity < worst) return WISE_ERR_INVALID_ARG;
+  if (workspace_bytes < support_workspace_bytes(bh, nq)) return WISE_ERR_INVALID_ARG;
+  hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, row_ptr, col_idx, nnz, workspace,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
+}
+
+wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
+                             const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity, float scale,
+                             void* stream) {
+  wise_status st = check_attn_shape(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
+  if (st != WISE_OK) return st;
+  if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
+  if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
+  return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, nullptr, row_ptr, col_idx, col_capacity,
+                  true, scale, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+"""Thin ctypes binding of libwise.so (C ABI in include/wise.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch supplies device memory (output tensors are allocated here when
+the caller passes none) and the current HIP stream.  If the library is missing
+or fails to load, importing this module raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwise.so")
+
+WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
+WISE_BF16, WISE_FP32 = 0, 1
+BLOCK = 32
+
+EXPORTED = (
+    "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_dense_attn",
+    "wise_build_support_workspace_bytes", "wise_build_support", "wise_sparse_attn",
+)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_sparse_attention_wise_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+    lib.wise_abi_version.restype = i32
+    lib.wise_status_string.restype = ctypes.c_char_p
+    lib.wise_status_string.argtypes = [i32]
+    lib.wise_full_attn_mass.restype = i32
+    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_dense_attn.restype = i32
+    lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
+    lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.wise_build_support.restype = i32
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
+    lib.wise_sparse_attn.restype = i32
+    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, f32, vp]
+    return lib
+
+
+lib = _load()
+
+
+class WiseError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib.wise_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != WISE_OK:
+        raise WiseError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return WISE_BF16
+    if t.dtype == torch.float32:
+        return WISE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _qkv_shape(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, seqlen, head_dim]")
+    for t in (q, k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    return q.shape
+
+
+def _out_like(q, out):
+    if out is None:
+        return torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must match q")
+    return out
+
+
+def _f32_buf(t, numel, device, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < numel or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 device tensor with >= {numel} elements")
+    return t
+
+
+def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, want_mass=False,
+                   scale=None, block=BLOCK, stream=None):
+    """Causal attention O (and optionally row LSE and block masses [b*h, nq, nq]).
+
+    Returns (out, lse, mass); lse / mass are None unless passed or requested.
+    """
+    b, h, n, d = _qkv_shape(q, k, v)
+    out = _out_like(q, out)
+    nq = n // block
+    if want_lse and lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    if want_mass and mass is None:
+        mass = torch.empty((b * h, nq, nq), dtype=torch.float32, device=q.device)
+    lse = _f32_buf(lse, b * h * n, q.device, "lse")
+    mass = _f32_buf(mass, b * h * nq * nq, q.device, "mass")
+    st = lib.wise_full_attn_mass(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _ptr(lse), _ptr(mass), float(scale or 0.0), _stream(stream))
+    _check(st, "wise_full_attn_mass")
+    return out, lse, mass
+
+
+def dense_attn(q, k, v, *, out=None, lse=None, want_lse=False, scale=None, block=BLOCK, stream=None):
+    """Dense causal attention (the in-run baseline).  Returns (out, lse)."""
+    b, h, n, d = _qkv_shape(q, k, v)
+    out = _out_like(q, out)
+    if want_lse and lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    lse = _f32_buf(lse, b * h * n, q.device, "lse")
+    st = lib.wise_dense_attn(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                             _ptr(lse), float(scale or 0.0), _stream(stream))
+    _check(st, "wise_dense_attn")
+    return out, lse
+
+
+def build_support_workspace_bytes(bh: int, nq: int, num_steps: int) -> int:
+    return int(lib.wise_build_support_workspace_bytes(bh, nq, num_steps))
+
+
+class Schedule:
+    """Device-resident CSR schedule: row_ptr [rows+1], col_idx [capacity], nnz [1] (int32)."""
+
+    def __init__(self, row_ptr, col_idx, nnz, bh, nq):
+        self.row_ptr, self.col_idx, self.nnz, self.bh, self.nq = row_ptr, col_idx, nnz, bh, nq
+
+
+def alloc_schedule(bh: int, nq: int, device):
+    cap = bh * nq * (nq + 1) // 2
+    return Schedule(torch.empty(bh * nq + 1, dtype=torch.int32, device=device),
+                    torch.empty(max(cap, 1), dtype=torch.int32, device=device),
+                    torch.empty(1, dtype=torch.int32, device=device), bh, nq)
+
+
+def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspace=None, stream=None):
+    """Selection + temporal union + CSR from masses [num_steps, b*h, nq, nq] (fp32)."""
+    if mass.dim() != 4 or mass.shape[2] != mass.shape[3]:
+        raise ValueError("mass must be [num_steps, batch*heads, nq, nq]")
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
+        raise ValueError("mass must be a contiguous float32 device tensor")
+    steps, bh, nq, _ = mass.shape
+    if schedule is None:
+        schedule = alloc_schedule(bh, nq, mass.device)
+    need = build_support_workspace_bytes(bh, nq, steps)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=mass.device)
+    st = lib.wise_build_support(bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
+                                _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "wise_build_support")
+    return schedule
+
+
+def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=False, scale=None,
+                block=BLOCK, stream=None):
+    """Block-sparse causal attention over a CSR schedule.  Returns (out, lse)."""
+    b, h, n, d = _qkv_shape(q, k, v)
+    out = _out_like(q, out)
+    if want_lse and lse is None:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+    lse = _f32_buf(lse, b * h * n, q.device, "lse")
+    for t in (schedule.row_ptr, schedule.col_idx):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("schedule tensors must be contiguous int32 on q's device")
+    if schedule.row_ptr.numel() < b * h * (n // block) + 1:
+        raise ValueError("row_ptr too short for this shape")
+    st = lib.wise_sparse_attn(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                              _ptr(lse), _ptr(schedule.row_ptr), _ptr(schedule.col_idx),
+                              schedule.col_idx.numel(), float(scale or 0.0), _stream(stream))
+    _check(st, "wise_sparse_attn")
+    return out, lse

@@ -1,0 +1,142 @@
+/*
+ * wise.h -- C ABI of the WISE working-set attention library (libwise.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow Wan & Chen, "Attention Routing Stabilizes Early:
+ * Working-Set Inference for Recurrent-Depth Language Models" (arXiv 2609.27373),
+ * cited below as "the WISE paper".  A recurrent-depth model recomputes causal
+ * attention at every recurrent step; WISE runs full attention in early steps,
+ * records per-(head, query block) block masses in steps 9..12, keeps for each
+ * step the smallest set of key blocks reaching mass eta, unions the sets into a
+ * CSR schedule once, and runs block-sparse attention over that schedule on the
+ * fresh Q/K/V of steps 13..32.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are batch-major, head-major, row-major: q, k, v, o are
+ *     [batch][heads][seqlen][head_dim] contiguous; "row" r = (b*heads + h)*nq + qb
+ *     indexes a (batch, head, query block) triple, nq = seqlen / block.
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, 16-byte
+ *     aligned.  The library allocates nothing and keeps no state between calls,
+ *     so concurrent calls on different streams are safe.
+ *   - stream is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *     Calls enqueue work and return without synchronising.
+ *   - Arguments are validated on the host before any HIP call.  On an invalid
+ *     argument nothing is launched and WISE_ERR_INVALID_ARG (or
+ *     WISE_ERR_UNSUPPORTED for a valid but unimplemented shape) is returned.
+ *     WISE_ERR_HIP reports a failed launch.
+ *   - Only block = 32 and head_dim in {64, 128} are implemented; seqlen must be a
+ *     positive multiple of block.  scale <= 0 selects 1/sqrt(head_dim).
+ */
+#ifndef WISE_H_
+#define WISE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WISE_OK = 0,
+  WISE_ERR_INVALID_ARG = 1,
+  WISE_ERR_UNSUPPORTED = 2,
+  WISE_ERR_HIP = 3
+} wise_status;
+
+typedef enum {
+  WISE_BF16 = 0, /* bf16 inputs/outputs, fp32 accumulation on bf16 MFMA */
+  WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
+} wise_dtype;
+
+#define WISE_ABI_VERSION 1
+
+int wise_abi_version(void);
+const char* wise_status_string(wise_status s);
+
+/*
+ * Full causal attention of a discovery step, with optional block-mass epilogue.
+ *
+ * Computes O = softmax(Q K^T * scale + M) V with the causal mask M (key j is
+ * admissible for query i iff j <= i) -- the WISE paper, §3, recurrent attention.
+ *   q, k, v, o : [batch][heads][seqlen][head_dim] of dtype dt; o is written.
+ *   lse        : NULL, or fp32 [batch*heads*seqlen] receiving the natural-log
+ *                log-sum-exp of every query row's scaled logits.
+ *   mass       : NULL, or fp32 [batch*heads][nq][nq] receiving the block mass of
+ *                the WISE paper §5.1 (Eq. 5):
+ *                  mass[bh][q][b] = (1/block) sum_{i in query block q}
+ *                                   sum_{j in key block b, j <= i} A_ij,
+ *                with A the attention probabilities above; entries b > q are 0.
+ *                The masses are computed from fp32 probabilities in a second
+ *                sweep over the keys once each row's log-sum-exp is known.
+ * With mass == NULL this is the dense baseline kernel.
+ */
+wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
+                                int block, const void* q, const void* k, const void* v, void* o,
+                                float* lse, float* mass, float scale, void* stream);
+
+/* Dense causal attention: wise_full_attn_mass with mass = NULL. */
+wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
+                            int block, const void* q, const void* k, const void* v, void* o,
+                            float* lse, float scale, void* stream);
+
+/*
+ * Bytes of device workspace wise_build_support needs for bh = batch*heads rows of
+ * nq query blocks and num_steps discovery steps (0 on invalid sizes).
+ */
+size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
+
+/*
+ * Working-set schedule construction (one-time, after the discovery steps).
+ *
+ * For every row (bh, q) and every step t < num_steps, the admissible key blocks
+ * b = 0..q are ordered by (mass descending, block index ascending) and the
+ * smallest prefix whose fp64 cumulative mass reaches eta is kept (the
+ * cumulative-eta support of the WISE paper, §3 and §5.1); eta >= 1, or a sum
+ * that never reaches eta, keeps every admissible block.  The per-step sets are
+ * unioned over the steps (the temporal union of the WISE paper, App. B, WISE
+ * configuration: steps t_d-3 .. t_d) and emitted as the CSR schedule of the WISE
+ * paper, App. B (sparse-kernel implementation):
+ *   mass        : fp32 [num_steps][bh][nq][nq] as written by wise_full_attn_mass
+ *                 (only entries b <= q are read).
+ *   eta         : cumulative-mass threshold, 0 < eta <= 1.
+ *   row_ptr     : int32 [bh*nq + 1], written; row r's blocks are
+ *                 col_idx[row_ptr[r] .. row_ptr[r+1]).
+ *   col_idx     : int32 [col_capacity], written; ascending within a row.
+ *   col_capacity: must be >= bh*nq*(nq+1)/2 (the fully dense worst case).
+ *   nnz         : int32 device scalar, written with row_ptr[bh*nq].
+ *   workspace   : device scratch of at least
+ *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
+ *                 its contents on entry do not matter.
+ * Requires 1 <= num_steps <= 64 and 1 <= nq <= 4096.
+ */
+wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                               int32_t* nnz, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Late-step block-sparse causal attention over a CSR schedule.
+ *
+ * O = softmax(Q K^T * scale + M + R) V, where R_ij = 0 if key block b(j) is
+ * listed for the query block of i and -inf otherwise (the reuse mask of the WISE
+ * paper, §5.2): the softmax renormalises over the scheduled keys.  Blocks absent
+ * from the schedule are skipped, not masked.  Fresh q, k, v every call.
+ *   q, k, v, o, lse, scale : as for wise_full_attn_mass (lse may be NULL).
+ *   row_ptr, col_idx       : the schedule (as produced by wise_build_support),
+ *                            rows ordered (b*heads + h)*nq + q.
+ *   col_capacity           : number of readable col_idx entries.
+ * Entries outside 0..q, and offsets outside 0..col_capacity, are ignored.  A row
+ * left with no admissible key writes o = 0 and lse = -inf (wise_build_support
+ * never produces one).
+ */
+wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
+                             int block, const void* q, const void* k, const void* v, void* o,
+                             float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                             int64_t col_capacity, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WISE_H_ */

@@ -42,7 +42,7 @@ def _scale(d: int, scale) -> float:
     return 1.0 / np.sqrt(d) if scale is None else float(scale)
 
 
-def causal_attention(q, k, v, scale=None):
+def causal_attention(q, k, v, scale=None, rows=None):
     """Full causal attention of one head.
 
     The WISE paper, §3 "Recurrent attention": A = softmax(Q K^T / sqrt(d_h) + M),
@@ -50,24 +50,26 @@ def causal_attention(q, k, v, scale=None):
     Written as the two-pass stable softmax: m_i = max_j s_ij, p_ij = exp(s_ij - m_i),
     l_i = sum_j p_ij, O_i = sum_j p_ij v_j / l_i, lse_i = m_i + log l_i.
 
-    q, k, v: [n, d].  Returns (O [n, d], lse [n]) in float64.
+    q, k, v: [n, d].  rows: optional (r0, r1) query-row range (default all rows).
+    Returns (O [r1 - r0, d], lse [r1 - r0]) in float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n, d = q.shape
+    lo, hi = (0, n) if rows is None else rows
     s = _scale(d, scale)
-    out = np.empty((n, v.shape[1]))
-    lse = np.empty(n)
-    for r0 in range(0, n, _ROW_CHUNK):
-        r1 = min(n, r0 + _ROW_CHUNK)
+    out = np.empty((hi - lo, v.shape[1]))
+    lse = np.empty(hi - lo)
+    for r0 in range(lo, hi, _ROW_CHUNK):
+        r1 = min(hi, r0 + _ROW_CHUNK)
         logits = (q[r0:r1] @ k.T) * s
-        rows = np.arange(r0, r1)[:, None]
-        cols = np.arange(n)[None, :]
-        logits[cols > rows] = -np.inf
+        ri = np.arange(r0, r1)[:, None]
+        cj = np.arange(n)[None, :]
+        logits[cj > ri] = -np.inf
         m = logits.max(axis=1, keepdims=True)
         p = np.exp(logits - m)
         l = p.sum(axis=1, keepdims=True)
-        out[r0:r1] = (p @ v) / l
-        lse[r0:r1] = m[:, 0] + np.log(l[:, 0])
+        out[r0 - lo:r1 - lo] = (p @ v) / l
+        lse[r0 - lo:r1 - lo] = m[:, 0] + np.log(l[:, 0])
     return out, lse
 
 
@@ -88,26 +90,28 @@ def attention_probs(q, k, scale=None, rows=None):
     return p / p.sum(axis=1, keepdims=True)
 
 
-def block_mass(q, k, block=32, scale=None):
+def block_mass(q, k, block=32, scale=None, qblocks=None):
     """Block-level attention mass of one head, the WISE paper §5.1 (Eq. 5).
 
     r_qb = (1/|I_q|) * sum_{i in I_q} sum_{j in I_b} A_ij, where I_q are the B rows
     of query block q and I_b the B keys of key block b.  A_ij = 0 for j > i, so
-    r_qb = 0 for b > q.  Returns r [nq, nq] in float64.
+    r_qb = 0 for b > q.  qblocks: optional (q0, q1) query-block range.
+    Returns r [q1 - q0, nq] in float64 (all nq query blocks by default).
     """
     q, k = _f64(q), _f64(k)
     n = q.shape[0]
     if n % block:
         raise ValueError("sequence length must be a multiple of the block size")
     nq = n // block
-    r = np.zeros((nq, nq))
+    q0, q1 = (0, nq) if qblocks is None else qblocks
+    r = np.zeros((q1 - q0, nq))
     rows_per_chunk = max(block, (_ROW_CHUNK // block) * block)
-    for r0 in range(0, n, rows_per_chunk):
-        r1 = min(n, r0 + rows_per_chunk)
+    for r0 in range(q0 * block, q1 * block, rows_per_chunk):
+        r1 = min(q1 * block, r0 + rows_per_chunk)
         a = attention_probs(q, k, scale, rows=(r0, r1))        # [rows, n]
         per_key_block = a.reshape(r1 - r0, nq, block).sum(axis=2)  # sum over j in I_b
         per_query_block = per_key_block.reshape((r1 - r0) // block, block, nq).sum(axis=1)
-        r[r0 // block:r1 // block] = per_query_block / block  # mean over i in I_q
+        r[r0 // block - q0:r1 // block - q0] = per_query_block / block  # mean over i in I_q
     return r
 
 
@@ -182,7 +186,7 @@ def build_csr(supports):
     return row_ptr, col_idx
 
 
-def sparse_attention(q, k, v, supports, block=32, scale=None):
+def sparse_attention(q, k, v, supports, block=32, scale=None, qblocks=None):
     """Late-step attention restricted to a frozen block support.
 
     The WISE paper, §5.2: R_ij = 0 if b(j) is in B_q(i), -inf otherwise, added to
@@ -191,18 +195,21 @@ def sparse_attention(q, k, v, supports, block=32, scale=None):
 
     supports: list over query blocks of block-index arrays (entries b > q have no
     admissible key and change nothing).  A row left with no admissible key (only
-    possible for an empty support) gets O = 0 and lse = -inf.
-    Returns (O [n, d], lse [n]) in float64.
+    possible for an empty support) gets O = 0 and lse = -inf.  qblocks: optional
+    (q0, q1) query-block range; supports is still indexed by absolute query block.
+    Returns (O [rows, d], lse [rows]) in float64 for the rows of those blocks.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n, d = q.shape
     nq = n // block
+    q0, q1 = (0, nq) if qblocks is None else qblocks
     s = _scale(d, scale)
-    out = np.zeros((n, v.shape[1]))
-    lse = np.full(n, -np.inf)
+    out = np.zeros(((q1 - q0) * block, v.shape[1]))
+    lse = np.full((q1 - q0) * block, -np.inf)
     key_block = np.arange(n) // block
-    for qb in range(nq):
+    for qb in range(q0, q1):
         r0, r1 = qb * block, (qb + 1) * block
+        o0, o1 = r0 - q0 * block, r1 - q0 * block
         allowed_block = np.zeros(nq, dtype=bool)
         sup = np.asarray(supports[qb], dtype=np.int64)
         sup = sup[(sup >= 0) & (sup < nq)]
@@ -218,8 +225,8 @@ def sparse_attention(q, k, v, supports, block=32, scale=None):
         m = lg.max(axis=1, keepdims=True)
         p = np.exp(lg - m)
         l = p.sum(axis=1, keepdims=True)
-        out[r0:r1][live] = (p @ v) / l
-        lse[r0:r1][live] = m[:, 0] + np.log(l[:, 0])
+        out[o0:o1][live] = (p @ v) / l
+        lse[o0:o1][live] = m[:, 0] + np.log(l[:, 0])
     return out, lse
 
 

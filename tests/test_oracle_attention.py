@@ -169,3 +169,19 @@ def test_sparse_empty_support_convention():
     o, lse = O.sparse_attention(q, k, v, [np.array([], dtype=int), np.array([1])], block=32)
     assert np.all(o[:32] == 0.0) and np.all(np.isneginf(lse[:32]))
     assert np.all(np.isfinite(o[32:]))
+
+
+def test_row_subsets_equal_slices_of_the_whole():
+    n, d, block = 320, 16, 32
+    q, k, v = _qkv(n, d, 2.0)
+    o, lse = O.causal_attention(q, k, v)
+    o2, lse2 = O.causal_attention(q, k, v, rows=(64, 200))
+    # equal up to BLAS blocking order
+    np.testing.assert_allclose(o2, o[64:200], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse[64:200], rtol=1e-13, atol=1e-14)
+    sup = [np.nonzero(RNG.random(qb + 1) < 0.6)[0] for qb in range(n // block)]
+    sup = [s if s.size else np.array([qb]) for qb, s in enumerate(sup)]
+    so, sl = O.sparse_attention(q, k, v, sup, block=block)
+    so2, sl2 = O.sparse_attention(q, k, v, sup, block=block, qblocks=(3, 7))
+    np.testing.assert_allclose(so2, so[96:224], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(sl2, sl[96:224], rtol=1e-13, atol=1e-14)

@@ -93,3 +93,10 @@ def test_sum_of_block_mass_matches_attention_columns():
 def test_rejects_ragged_length():
     with pytest.raises(ValueError):
         O.block_mass(np.zeros((33, 4)), np.zeros((33, 4)), 32)
+
+
+def test_query_block_subset_equals_slice():
+    n, d = 640, 16
+    q, k = RNG.standard_normal((n, d)) * 2, RNG.standard_normal((n, d)) * 2
+    r = O.block_mass(q, k, 32)
+    np.testing.assert_allclose(O.block_mass(q, k, 32, qblocks=(5, 19)), r[5:19], rtol=1e-13, atol=1e-15)
