@@ -108,6 +108,8 @@ struct RowState {
   }
 };
 
+constexpr float kSlack = 8.f;  // log2 units
+
 // One key block: scores, causal mask on the diagonal block, online softmax, P V.
 template <int D, class QS>
 __device__ __forceinline__ void attend_block(RowState<D>& st, const bf16x8 (&kf)[Tile<D>::NC], const QS& qf,
@@ -122,19 +124,23 @@ __device__ __forceinline__ void attend_block(RowState<D>& st, const bf16x8 (&kf)
 #pragma unroll
   for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
   tmax = halves_max(tmax) * sl2;
-  const float m_new = fmaxf(st.m, tmax);
-  if (__ballot(m_new > st.m) != 0ull) {
+  // Lazy rescale: the subtracted max only has to bound the exponent, so it is
+  // raised (and O, l rescaled) only when some row's max exceeds it by more than
+  // kSlack; otherwise p <= 2^kSlack, exact in fp32 and fine for bf16 P.
+  if (__ballot(tmax > st.m + kSlack) != 0ull) {
+    const float m_new = fmaxf(st.m, tmax);
     const float alpha = fast_exp2(st.m - m_new);
     st.l *= alpha;
 #pragma unroll
     for (int t = 0; t < Tile<D>::NT; ++t) st.acc[t] *= alpha;
     st.m = m_new;
   }
+  const float m_use = st.m;
   float psum = 0.f;
   bf16x8 pb[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p = fast_exp2(fmaf(s[r], sl2, -m_new));
+    const float p = fast_exp2(fmaf(s[r], sl2, -m_use));
     psum += p;
     pb[r >> 3][r & 7] = (__bf16)p;
   }
@@ -168,67 +174,177 @@ __device__ __forceinline__ float finish_rows(const RowState<D>& st, __bf16* orow
   return lse2;
 }
 
-// ------------------------------------------------------------------ dense
+// ------------------------------------------------------------------ streaming kernel
+//
+// One 4-wavefront workgroup owns 4 consecutive query blocks q0..q0+3 of one
+// (batch, head); wavefront w owns query block q0 + w.  The workgroup streams a
+// list of key blocks through double-buffered LDS tiles shared by its
+// wavefronts, and every wavefront runs the key-block step on the blocks of its
+// own row:
+//   dense   list = 0 .. q0+3, wavefront w takes b <= q0 + w;
+//   sparse  list = union of the 4 rows' scheduled blocks (ascending), wavefront
+//           w takes the blocks of its own CSR row.
+// Neighbouring query blocks share key blocks (the sink, recent context), so the
+// sparse union reads each shared block once per workgroup.  Global loads run two
+// blocks ahead of the compute through two register staging sets.
 
-template <int D, bool MASS>
-__global__ __launch_bounds__(256) void attn_dense_kernel(AttnBf16Args a) {
+constexpr int kWaves = 4;
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left free
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+constexpr int kMaxMaskWords = 128;  // sparse rows: nq <= 4096
+
+enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2 };
+
+// Key-block lists; next() is wave-uniform (scalar) control flow.
+struct DenseList {
+  int b, nb;
+  __device__ __forceinline__ int next() { return b < nb ? b++ : -1; }
+};
+struct UnionList {
+  const uint32_t* masks;  // [kWaves][kMaxMaskWords] in LDS
+  int nwords, wd;
+  uint32_t u;
+  __device__ __forceinline__ uint32_t word(int w) const {
+    return __builtin_amdgcn_readfirstlane(masks[w] | masks[kMaxMaskWords + w] | masks[2 * kMaxMaskWords + w] |
+                                          masks[3 * kMaxMaskWords + w]);
+  }
+  __device__ __forceinline__ int next() {
+    while (u == 0u) {
+      if (++wd >= nwords) return -1;
+      u = word(wd);
+    }
+    const int bit = __builtin_ctz(u);
+    u &= u - 1u;
+    return 32 * wd + bit;
+  }
+};
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void attn_stream_kernel(AttnBf16Args a) {
   using T = Tile<D>;
   constexpr int CPT = (32 * T::C8) / 256;  // 16-byte chunks of one tile per thread
+  constexpr bool SPARSE = MODE == kSparse;
   __shared__ __attribute__((aligned(16))) __bf16 kt[2][32 * T::KSTRIDE];
   __shared__ __attribute__((aligned(16))) __bf16 vt[2][32 * T::VSTRIDE];
+  __shared__ uint32_t rmask[SPARSE ? kWaves * kMaxMaskWords : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 31, h = lane >> 5;
-  const int ngroups = (a.nq + 3) >> 2;
+  const int ngroups = (a.nq + kWaves - 1) / kWaves;
   const int bhn = a.rows / a.nq;
-  const int logical = xcd_remap(blockIdx.x, bhn * ngroups);
-  const int bh = logical / ngroups;
-  const int grp = ngroups - 1 - (logical - bh * ngroups);  // longest groups of a head first
-  const int qb = 4 * grp + wave;
+  // Longest-first order over all heads: workgroup p takes the (p / bhn)-th longest
+  // query group of head p % bhn.  Consecutive workgroups land on different XCDs,
+  // so each XCD sees the heads congruent to it modulo 8 (bhn a multiple of 8).
+  const int bh = blockIdx.x % bhn;
+  const int grp = ngroups - 1 - (int)(blockIdx.x / bhn);
+  const int q0 = kWaves * grp;
+  const int qb = q0 + wave;
   const bool active = qb < a.nq;
-  const int nb = min(4 * grp + 4, a.nq);                   // key blocks streamed by this group
+  const int qlast = min(q0 + kWaves, a.nq) - 1;
   const size_t head_off = (size_t)bh * a.seqlen * D;
   const __bf16* kh = a.k + head_off;
   const __bf16* vh = a.v + head_off;
 
+  // Q^T operand; inactive wavefronts (past the last query block) read a valid row
+  // and discard it, so the load is unconditional and completes before the loop
+  // (keeping the in-loop waits on the prefetched K/V tiles only).
   QRegs<D> qf;
-  if (active) load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * qb + i) * D, h);
+  load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * min(qb, a.nq - 1) + i) * D, h);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  if (SPARSE) {
+    // this wavefront's row as a bitmask over key blocks (entries outside 0..qb
+    // and offsets outside 0..col_cap are ignored; duplicates count once)
+    const int nwords = (qlast >> 5) + 1;
+    uint32_t* my = rmask + wave * kMaxMaskWords;
+    for (int w = lane; w < nwords; w += 64) my[w] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (active) {
+      const int row = bh * a.nq + qb;
+      int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
+      b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
+      b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
+      for (int64_t e = b0 + lane; e < b1; e += 64) {
+        const int b = a.col_idx[e];
+        if (b >= 0 && b <= qb) atomicOr(&my[b >> 5], 1u << (b & 31));
+      }
+    }
+    __syncthreads();
+  }
 
   // cooperative tile copy: chunk c = tid + 256*u -> row c / C8, column chunk c % C8
-  bf16x8 kr[CPT], vr[CPT];
-  auto gload = [&](int b, bool with_v) {
+  struct Stage {
+    bf16x8 k[CPT], v[CPT];
+  };
+  auto gload = [&](Stage& r, int b, bool with_v) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = tid + 256 * u;
       const size_t off = (size_t)(32 * b + c / T::C8) * D + (c % T::C8) * 8;
-      kr[u] = *reinterpret_cast<const bf16x8*>(kh + off);
-      if (with_v) vr[u] = *reinterpret_cast<const bf16x8*>(vh + off);
+      r.k[u] = *reinterpret_cast<const bf16x8*>(kh + off);
+      if (with_v) r.v[u] = *reinterpret_cast<const bf16x8*>(vh + off);
     }
   };
-  auto lstore = [&](int buf, bool with_v) {
+  auto lstore = [&](const Stage& r, int buf, bool with_v) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = tid + 256 * u;
-      *reinterpret_cast<bf16x8*>(&kt[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = kr[u];
-      if (with_v) *reinterpret_cast<bf16x8*>(&vt[buf][(c / T::C8) * T::VSTRIDE + (c % T::C8) * 8]) = vr[u];
+      *reinterpret_cast<bf16x8*>(&kt[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = r.k[u];
+      if (with_v) *reinterpret_cast<bf16x8*>(&vt[buf][(c / T::C8) * T::VSTRIDE + (c % T::C8) * 8]) = r.v[u];
+    }
+  };
+  auto member = [&](int b) -> bool {
+    if (!SPARSE) return active && b <= qb;
+    return (__builtin_amdgcn_readfirstlane(rmask[wave * kMaxMaskWords + (b >> 5)]) >> (b & 31)) & 1u;
+  };
+
+  // Runs `work(b, buf)` over the list, two blocks per trip: the trip's two
+  // tiles sit in LDS buffers 0 and 1 while the next two are fetched into the
+  // register stages; every load is waited for inside the trip it was issued in,
+  // so the compiler's wait counts stay exact across the loop back-edge.
+  auto stream = [&](auto& list, bool with_v, auto&& work) {
+    Stage ra, rb;
+    int c0 = list.next();
+    int c1 = c0 >= 0 ? list.next() : -1;
+    if (c0 >= 0) gload(ra, c0, with_v);
+    if (c1 >= 0) gload(rb, c1, with_v);
+    if (c0 >= 0) lstore(ra, 0, with_v);
+    if (c1 >= 0) lstore(rb, 1, with_v);
+    __syncthreads();
+    while (c0 >= 0) {
+      const int n0 = c1 >= 0 ? list.next() : -1;
+      const int n1 = n0 >= 0 ? list.next() : -1;
+      if (n0 >= 0) gload(ra, n0, with_v);
+      if (n1 >= 0) gload(rb, n1, with_v);
+      work(c0, 0);
+      if (c1 >= 0) work(c1, 1);
+      __syncthreads();
+      if (n0 >= 0) lstore(ra, 0, with_v);
+      if (n1 >= 0) lstore(rb, 1, with_v);
+      __syncthreads();
+      c0 = n0;
+      c1 = n1;
     }
   };
 
   RowState<D> st;
   st.init();
-  gload(0, true);
-  lstore(0, true);
-  __syncthreads();
-  for (int b = 0; b < nb; ++b) {
-    const int buf = b & 1;
-    if (b + 1 < nb) gload(b + 1, true);
-    if (active && b <= qb) {
+  auto attend = [&](int b, int buf) {
+    if (member(b)) {
       bf16x8 kf[T::NC];
       load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
       attend_block<D>(st, kf, qf, vt[buf], b == qb, i, h, lane, a.scale_log2);
     }
-    if (b + 1 < nb) lstore(buf ^ 1, true);
-    __syncthreads();
+  };
+  if (SPARSE) {
+    UnionList list{rmask, (qlast >> 5) + 1, 0, 0u};
+    list.u = list.word(0);
+    stream(list, true, attend);
+  } else {
+    DenseList list{0, qlast + 1};
+    stream(list, true, attend);
   }
 
   float lse2 = -INFINITY;
@@ -237,16 +353,12 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnBf16Args a) {
     lse2 = finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
   }
 
-  if (MASS) {
+  if (MODE == kDenseMass) {
     // Block mass (Eq. 5): r_qb = (1/32) sum_i sum_{j in b, j <= i} exp(s_ij - lse_i),
     // a second sweep over the keys now that every row's log-sum-exp is final.
     float* mrow = a.mass + (size_t)(bh * a.nq + qb) * a.nq;
-    gload(0, false);
-    lstore(0, false);
-    __syncthreads();
-    for (int b = 0; b < nb; ++b) {
-      const int buf = b & 1;
-      if (b + 1 < nb) gload(b + 1, false);
+    DenseList list{0, qlast + 1};
+    stream(list, false, [&](int b, int buf) {
       if (active && b <= qb) {
         bf16x8 kf[T::NC];
         load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
@@ -261,200 +373,31 @@ __global__ __launch_bounds__(256) void attn_dense_kernel(AttnBf16Args a) {
         const float tot = wave_sum(part);
         if (lane == 0) mrow[b] = tot * (1.f / 32.f);
       }
-      if (b + 1 < nb) lstore(buf ^ 1, false);
-      __syncthreads();
-    }
+    });
     if (active)
       for (int b = qb + 1 + lane; b < a.nq; b += 64) mrow[b] = 0.f;
   }
 }
 
-// ------------------------------------------------------------------ sparse
-
-// Walks one CSR row's valid entries (0 <= b <= qb), 64 entries at a time held one
-// per lane; the valid mask is wave-uniform, so next() is scalar control flow.
-struct RowCursor {
-  const int32_t* col;
-  int base, end, qb, lane;
-  int cur;          // this lane's entry of the current chunk
-  uint64_t mask;    // valid, not yet returned entries of the current chunk
-  __device__ __forceinline__ void load_chunk() {
-    const int e = base + lane;
-    cur = e < end ? col[e] : -1;
-    mask = __ballot(cur >= 0 && cur <= qb);
-  }
-  __device__ __forceinline__ int next() {
-    while (mask == 0ull) {
-      base += 64;
-      if (base >= end) return -1;
-      load_chunk();
-    }
-    const int j = __builtin_ctzll(mask);
-    mask &= mask - 1;
-    return __builtin_amdgcn_readlane(cur, j);
-  }
-  // the valid entry after skipping `skip` valid entries (-1 at the end)
-  __device__ __forceinline__ int next_after(int skip) {
-    for (int s = 0; s < skip; ++s)
-      if (next() < 0) return -1;
-    return next();
-  }
-};
-
-// S wavefronts share one (head, query block) row: wavefront w takes the valid
-// scheduled blocks w, w+S, w+2S, ... with its own online-softmax state, and the
-// states are merged through LDS at the end.  This shortens the serial chain of
-// the longest rows and puts S blocks of one row in flight at once.
-template <int D, int S>
-__global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_sparse_kernel(AttnBf16Args a) {
-  using T = Tile<D>;
-  constexpr int VTILE = 32 * T::VSTRIDE;                 // elements of one wavefront's V tile
-  constexpr int MERGE_FLOATS = (T::NT * 16 + 2) * 64;    // one wavefront's state, lane-major
-  constexpr int LDS_BYTES = (S * VTILE * 2 > (S - 1) * MERGE_FLOATS * 4) ? S * VTILE * 2 : (S - 1) * MERGE_FLOATS * 4;
-  constexpr int QTILE = 32 * T::KSTRIDE;                  // elements of one wavefront's Q tile
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES + S * QTILE * 2];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int i = lane & 31, h = lane >> 5;
-  const int logical = xcd_remap(blockIdx.x, a.rows);
-  const int bh = logical / a.nq;
-  const int qb = a.nq - 1 - (logical - bh * a.nq);  // longest rows of a head first
-  const int row = bh * a.nq + qb;
-  const size_t head_off = (size_t)bh * a.seqlen * D;
-  const __bf16* kh = a.k + head_off;
-  const __bf16* vh = a.v + head_off;
-  __bf16* vt = reinterpret_cast<__bf16*>(lds) + wave * VTILE;
-  __bf16* qt = reinterpret_cast<__bf16*>(lds + LDS_BYTES) + wave * QTILE;
-
-  // Q tile -> LDS (same coalesced pattern as the V copies below)
-  {
-    constexpr int RPI = 64 / T::C8;
-    const __bf16* src = a.q + head_off + (size_t)(32 * qb + lane / T::C8) * D + 8 * (lane % T::C8);
-    __bf16* dst = qt + (lane / T::C8) * T::KSTRIDE + 8 * (lane % T::C8);
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c)
-      *reinterpret_cast<bf16x8*>(dst + RPI * c * T::KSTRIDE) = *reinterpret_cast<const bf16x8*>(src + (size_t)(RPI * c) * D);
-  }
-  const QLds<D> qf{qt + i * T::KSTRIDE + h * T::HALF};
-
-  int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
-  b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
-  b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
-  RowCursor cur{a.col_idx, (int)b0, (int)b1, qb, lane, -1, 0ull};
-  if (cur.base < cur.end) cur.load_chunk();
-
-  // V copy: instruction c moves rows (64/C8)*c + lane/C8, 16-byte chunk lane%C8 --
-  // contiguous 1 KB per instruction in global memory, and 16 consecutive lanes
-  // fill one 256-byte LDS row (no bank conflicts at D = 128).
-  constexpr int RPI = 64 / T::C8;
-  const int vrow0 = lane / T::C8, vch = lane % T::C8;
-  auto vload = [&](bf16x8 (&vr)[T::NC], int b) {
-    const __bf16* base = vh + (size_t)(32 * b + vrow0) * D + 8 * vch;
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c) vr[c] = *reinterpret_cast<const bf16x8*>(base + (size_t)(RPI * c) * D);
-  };
-  auto vstore = [&](const bf16x8 (&vr)[T::NC]) {
-    __bf16* base = vt + vrow0 * T::VSTRIDE + 8 * vch;
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c) *reinterpret_cast<bf16x8*>(base + RPI * c * T::VSTRIDE) = vr[c];
-  };
-
-  RowState<D> st;
-  st.init();
-  bf16x8 ka[T::NC], kb[T::NC], vr[T::NC];
-  int b = cur.next_after(wave);
-  if (b >= 0) {
-    load_frag<D>(ka, kh + (size_t)(32 * b + i) * D, h);
-    vload(vr, b);
-  }
-  while (b >= 0) {
-    const int bn = cur.next_after(S - 1);
-    __builtin_amdgcn_wave_barrier();
-    vstore(vr);
-    if (bn >= 0) {
-      load_frag<D>(kb, kh + (size_t)(32 * bn + i) * D, h);
-      vload(vr, bn);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    attend_block<D>(st, ka, qf, vt, b == qb, i, h, lane, a.scale_log2);
-    if (bn < 0) break;
-    b = cur.next_after(S - 1);
-    __builtin_amdgcn_wave_barrier();
-    vstore(vr);
-    if (b >= 0) {
-      load_frag<D>(ka, kh + (size_t)(32 * b + i) * D, h);
-      vload(vr, b);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    attend_block<D>(st, kb, qf, vt, bn == qb, i, h, lane, a.scale_log2);
-  }
-
-  if (S > 1) {
-    // merge: wavefronts 1..S-1 publish (acc, m, l) lane-major, wavefront 0 combines
-    __syncthreads();
-    float* ms = reinterpret_cast<float*>(lds);
-    if (wave > 0) {
-      float* dst = ms + (wave - 1) * MERGE_FLOATS + lane;
-#pragma unroll
-      for (int t = 0; t < T::NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(t * 16 + r) * 64] = st.acc[t][r];
-      dst[(T::NT * 16) * 64] = st.m;
-      dst[(T::NT * 16 + 1) * 64] = st.l;
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    float m_all = st.m;
-    for (int w = 1; w < S; ++w) m_all = fmaxf(m_all, ms[(w - 1) * MERGE_FLOATS + (T::NT * 16) * 64 + lane]);
-    const float f0 = st.m == -INFINITY ? 0.f : fast_exp2(st.m - m_all);
-    st.l *= f0;
-#pragma unroll
-    for (int t = 0; t < T::NT; ++t) st.acc[t] *= f0;
-    for (int w = 1; w < S; ++w) {
-      const float* src = ms + (w - 1) * MERGE_FLOATS + lane;
-      const float mw = src[(T::NT * 16) * 64];
-      const float fw = mw == -INFINITY ? 0.f : fast_exp2(mw - m_all);
-      st.l += src[(T::NT * 16 + 1) * 64] * fw;
-#pragma unroll
-      for (int t = 0; t < T::NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.acc[t][r] += src[(t * 16 + r) * 64] * fw;
-    }
-    st.m = m_all;
-  }
-  float* lse_out = a.lse != nullptr ? a.lse + (size_t)bh * a.seqlen + 32 * qb + i : nullptr;
-  finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
-}
-
 // ------------------------------------------------------------------ launch
-
-#ifndef WISE_SPARSE_SPLIT
-#define WISE_SPARSE_SPLIT 2
-#endif
-constexpr int kSparseSplit = WISE_SPARSE_SPLIT;  // wavefronts per sparse row
 
 hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream) {
   const int bhn = a.rows / a.nq;
-  const int dense_groups = bhn * ((a.nq + 3) / 4);
+  const dim3 grid(bhn * ((a.nq + kWaves - 1) / kWaves)), block(64 * kWaves);
   if (head_dim == 128) {
     if (sparse)
-      hipLaunchKernelGGL((attn_sparse_kernel<128, kSparseSplit>), dim3(a.rows), dim3(64 * kSparseSplit), 0, stream, a);
+      hipLaunchKernelGGL((attn_stream_kernel<128, kSparse>), grid, block, 0, stream, a);
     else if (mass)
-      hipLaunchKernelGGL((attn_dense_kernel<128, true>), dim3(dense_groups), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_stream_kernel<128, kDenseMass>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_dense_kernel<128, false>), dim3(dense_groups), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_stream_kernel<128, kDense>), grid, block, 0, stream, a);
   } else {
     if (sparse)
-      hipLaunchKernelGGL((attn_sparse_kernel<64, kSparseSplit>), dim3(a.rows), dim3(64 * kSparseSplit), 0, stream, a);
+      hipLaunchKernelGGL((attn_stream_kernel<64, kSparse>), grid, block, 0, stream, a);
     else if (mass)
-      hipLaunchKernelGGL((attn_dense_kernel<64, true>), dim3(dense_groups), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_stream_kernel<64, kDenseMass>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_dense_kernel<64, false>), dim3(dense_groups), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_stream_kernel<64, kDense>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -10,6 +10,7 @@ namespace wise {
 namespace {
 
 constexpr int kBlock = 32;
+constexpr int kMaxSparseBlocks = 4096;  // bf16 sparse kernel: key blocks per row bitmask
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -122,6 +123,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, in
   if (st != WISE_OK) return st;
   if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
   if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
+  if (dt == WISE_BF16 && seqlen / kBlock > kMaxSparseBlocks) return WISE_ERR_UNSUPPORTED;
   return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, nullptr, row_ptr, col_idx, col_capacity,
                   true, scale, stream);
 }

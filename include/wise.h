@@ -126,9 +126,11 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
  *   row_ptr, col_idx       : the schedule (as produced by wise_build_support),
  *                            rows ordered (b*heads + h)*nq + q.
  *   col_capacity           : number of readable col_idx entries.
- * Entries outside 0..q, and offsets outside 0..col_capacity, are ignored.  A row
- * left with no admissible key writes o = 0 and lse = -inf (wise_build_support
- * never produces one).
+ * Entries outside 0..q, and offsets outside 0..col_capacity, are ignored, and a
+ * block listed twice counts once.  A row left with no admissible key writes
+ * o = 0 and lse = -inf (wise_build_support never produces one).  The bf16 kernel
+ * supports up to 4096 key blocks per head (seqlen <= 131072); beyond that it
+ * returns WISE_ERR_UNSUPPORTED.
  */
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
                              int block, const void* q, const void* k, const void* v, void* o,
