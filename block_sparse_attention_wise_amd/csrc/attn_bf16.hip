@@ -73,17 +73,11 @@ __device__ __forceinline__ bf16x8 v_operand(const __bf16* vt, int t, int c2, int
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// Q^T operand sources: held in registers, or re-read from a padded LDS tile
-// (row stride KSTRIDE) every block to save 32 VGPRs per lane.
+// Q^T operand source: the query block's fragments held in registers.
 template <int D>
 struct QRegs {
   bf16x8 f[Tile<D>::NC];
   __device__ __forceinline__ bf16x8 get(int c) const { return f[c]; }
-};
-template <int D>
-struct QLds {
-  const __bf16* row;  // this lane's query row in LDS, offset to its half
-  __device__ __forceinline__ bf16x8 get(int c) const { return reinterpret_cast<const bf16x8*>(row)[c]; }
 };
 
 template <int D, class QS>
@@ -120,9 +114,13 @@ __device__ __forceinline__ void attend_block(RowState<D>& st, const bf16x8 (&kf)
     for (int r = 0; r < 16; ++r)
       if (acc_row(r, h) > i) s[r] = -INFINITY;
   }
-  float tmax = s[0];
+  // pairwise trees keep the dependent-instruction chains short
+  float mx[8];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+  for (int r = 0; r < 8; ++r) mx[r] = fmaxf(s[r], s[r + 8]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], mx[r + 4]);
+  float tmax = fmaxf(fmaxf(mx[0], mx[2]), fmaxf(mx[1], mx[3]));
   tmax = halves_max(tmax) * sl2;
   // Lazy rescale: the subtracted max only has to bound the exponent, so it is
   // raised (and O, l rescaled) only when some row's max exceeds it by more than
@@ -136,14 +134,18 @@ __device__ __forceinline__ void attend_block(RowState<D>& st, const bf16x8 (&kf)
     st.m = m_new;
   }
   const float m_use = st.m;
-  float psum = 0.f;
+  float pv[16];
   bf16x8 pb[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p = fast_exp2(fmaf(s[r], sl2, -m_use));
-    psum += p;
-    pb[r >> 3][r & 7] = (__bf16)p;
+    pv[r] = fast_exp2(fmaf(s[r], sl2, -m_use));
+    pb[r >> 3][r & 7] = (__bf16)pv[r];
   }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pv[r] += pv[r + 8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pv[r] += pv[r + 4];
+  const float psum = (pv[0] + pv[2]) + (pv[1] + pv[3]);
   st.l += psum;
 #pragma unroll
   for (int t = 0; t < Tile<D>::NT; ++t) {
