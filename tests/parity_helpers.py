@@ -31,6 +31,13 @@ def f64(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+def step_pair(gen, step, device="cuda"):
+    """(host, device) copies of one step's Q, K, V: the oracle reads the host
+    tensors the generator produced, the HIP path reads their device copies."""
+    host = gen.step_torch(step)
+    return host, tuple(x.to(device) for x in host)
+
+
 def assert_attn_close(gpu, ref, dtype, what):
     tol = TOL[dtype]
     err = np.abs(gpu - ref)

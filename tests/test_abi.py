@@ -1,0 +1,131 @@
+"""The C ABI of libwise.so on the CPU: every symbol declared in include/wise.h is
+exported, and every invalid argument is rejected by host-side validation before
+any HIP call (no GPU needed: no valid call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wise.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_wise_amd", "libwise.so")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
+BF16, FP32 = 0, 1
+P = ctypes.c_void_p(0x10000)      # a fake, 16-byte aligned device pointer: never dereferenced
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)    # 4-byte aligned, not 16
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wise_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libwise.so is not built (run python -m block_sparse_attention_wise_amd.build)")
+    lib = ctypes.CDLL(LIB)
+    vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
+    lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
+    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, f32, vp]
+    lib.wise_status_string.restype = ctypes.c_char_p
+    lib.wise_status_string.argtypes = [i32]
+    return lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"wise_full_attn_mass", "wise_dense_attn", "wise_build_support",
+                          "wise_build_support_workspace_bytes", "wise_sparse_attn",
+                          "wise_status_string", "wise_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in wise.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.wise_abi_version() == 1
+    for s in (OK, INVALID, UNSUPPORTED, HIPERR):
+        assert lib.wise_status_string(s)
+    assert lib.wise_status_string(99) == b"unknown status"
+
+
+def _attn(lib, dt=BF16, b=1, h=2, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, mass=None, scale=0.0):
+    return lib.wise_full_attn_mass(dt, b, h, n, d, blk, q, k, v, o, lse, mass, scale, None)
+
+
+def test_attention_validation(lib):
+    assert _attn(lib, dt=7) == INVALID
+    for kw in (dict(b=0), dict(h=0), dict(n=0), dict(d=0), dict(blk=0), dict(n=-32)):
+        assert _attn(lib, **kw) == INVALID, kw
+    for name in ("q", "k", "v", "o"):
+        assert _attn(lib, **{name: NULL}) == INVALID, name
+        assert _attn(lib, **{name: MIS}) == INVALID, name
+    assert _attn(lib, n=100) == INVALID                 # seqlen not a multiple of the block
+    assert _attn(lib, blk=64) == UNSUPPORTED
+    assert _attn(lib, blk=16) == UNSUPPORTED
+    assert _attn(lib, d=96) == UNSUPPORTED
+    assert _attn(lib, lse=ctypes.c_void_p(0x10002)) == INVALID
+    assert _attn(lib, mass=ctypes.c_void_p(0x10001)) == INVALID
+    assert _attn(lib, scale=float("nan")) == INVALID
+    assert _attn(lib, scale=float("inf")) == INVALID
+    assert lib.wise_dense_attn(BF16, 1, 1, 64, 128, 32, P, P, P, NULL, None, 0.0, None) == INVALID
+    assert lib.wise_dense_attn(FP32, 1, 1, 64, 96, 32, P, P, P, P2, None, 0.0, None) == UNSUPPORTED
+
+
+def test_workspace_bytes(lib):
+    f = lib.wise_build_support_workspace_bytes
+    assert f(0, 8, 4) == 0 and f(1, 0, 4) == 0 and f(1, 8, 0) == 0 and f(1, 8, 65) == 0
+    assert f(1, 4097, 4) == 0
+    # bitmask words per row plus one count per row, 256-byte aligned sections
+    def expect(bh, nq):
+        al = lambda x: (x + 255) // 256 * 256
+        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4)
+    for bh, nq in ((1, 8), (32, 128), (32, 512), (3, 33)):
+        assert f(bh, nq, 4) == expect(bh, nq)
+
+
+def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, ws=P2, wsb=None):
+    cap = bh * nq * (nq + 1) // 2 if cap is None else cap
+    wsb = lib.wise_build_support_workspace_bytes(bh, nq, steps) if wsb is None else wsb
+    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, ws, wsb, None)
+
+
+def test_build_support_validation(lib):
+    for kw in (dict(bh=0), dict(nq=0), dict(nq=5000), dict(steps=0), dict(steps=65)):
+        assert _build(lib, **kw) == INVALID, kw
+    for name in ("mass", "rp", "ci", "nnz", "ws"):
+        assert _build(lib, **{name: NULL}) == INVALID, name
+    assert _build(lib, ws=ctypes.c_void_p(0x10008)) == INVALID
+    assert _build(lib, mass=ctypes.c_void_p(0x10002)) == INVALID
+    for eta in (0.0, -0.5, 1.0001, float("nan")):
+        assert _build(lib, eta=eta) == INVALID, eta
+    assert _build(lib, cap=2 * 8 * 9 // 2 - 1) == INVALID
+    assert _build(lib, wsb=16) == INVALID
+    # a worst case beyond int32 row offsets is rejected
+    assert _build(lib, bh=1 << 20, nq=4096, cap=1 << 62, wsb=1 << 62) == INVALID
+
+
+def test_sparse_validation(lib):
+    def sp(**kw):
+        a = dict(dt=BF16, b=1, h=1, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, rp=P, ci=P, cap=10,
+                 scale=0.0)
+        a.update(kw)
+        return lib.wise_sparse_attn(a["dt"], a["b"], a["h"], a["n"], a["d"], a["blk"], a["q"], a["k"], a["v"],
+                                    a["o"], a["lse"], a["rp"], a["ci"], a["cap"], a["scale"], None)
+    assert sp(rp=NULL) == INVALID
+    assert sp(ci=NULL) == INVALID
+    assert sp(cap=-1) == INVALID
+    assert sp(rp=ctypes.c_void_p(0x10001)) == INVALID
+    assert sp(n=96 + 1) == INVALID
+    assert sp(d=256) == UNSUPPORTED
+    assert sp(n=32 * 4097) == UNSUPPORTED              # bf16 rows beyond 4096 key blocks
+    assert sp(q=MIS) == INVALID

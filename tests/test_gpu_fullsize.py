@@ -1,0 +1,99 @@
+"""GPU parity at the full workload sizes (4k headline, 16k stress), in the launch
+configuration bench.py times: every head runs on the GPU, and sampled heads and
+query blocks are compared with the fp64 oracle computed one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_attention_wise_amd.synthetic import WORKLOADS, Generator
+from parity_helpers import (assert_attn_close, assert_lse_close, assert_mass_close, csr_rows, f64, note,
+                            oracle_union_row, step_pair)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CASES = {
+    "4k": dict(heads=[0, 11, 22, 31], qblocks=None),                       # every query block of 4 heads
+    "16k": dict(heads=[0, 31], qblocks=[0, 1, 2, 77, 255, 256, 400, 510, 511]),
+}
+
+
+def _run_gpu(name):
+    from block_sparse_attention_wise_amd import wise
+    w = WORKLOADS[name]
+    g = Generator(w)
+    mass = torch.empty((4, w.heads, w.nq, w.nq), dtype=torch.float32, device=DEV)
+    host = {}
+    for si, t in enumerate((9, 10, 11, 12)):
+        hq, dq = step_pair(g, t)
+        note(f"{name} discovery step {t}")
+        wise.full_attn_mass(*dq, mass=mass[si])
+        host[t] = hq[:2]
+        del dq
+    return wise, w, g, mass, host
+
+
+@pytest.mark.parametrize("name", ["4k", "16k"])
+def test_fullsize_schedule_and_sparse_attention(name):
+    wise, w, g, mass, host = _run_gpu(name)
+    case = CASES[name]
+    qbs = case["qblocks"] if case["qblocks"] is not None else list(range(w.nq))
+    torch.cuda.synchronize()
+    gm = mass.cpu().numpy()
+    # oracle masses of the sampled rows, compared with the GPU's
+    orc = {}
+    for h in case["heads"]:
+        for t in (9, 10, 11, 12):
+            qh, kh = f64(host[t][0][0, h]), f64(host[t][1][0, h])
+            for qb in qbs:
+                r = O.block_mass(qh, kh, qblocks=(qb, qb + 1))[0]
+                orc[(h, t, qb)] = r
+                assert_mass_close(gm[t - 9, h, qb], r, w.dtype, f"{name} head {h} step {t} block {qb}")
+    (q13, k13, v13), dev13 = step_pair(g, 13)
+    for eta in w.etas:
+        note(f"{name} build eta={eta}")
+        sched = wise.build_support(mass, eta)
+        note(f"{name} sparse eta={eta}")
+        o, lse = wise.sparse_attn(*dev13, sched, want_lse=True)
+        torch.cuda.synchronize()
+        rows = csr_rows(sched.row_ptr, sched.col_idx)
+        assert int(sched.nnz.item()) == int(sched.row_ptr[-1].item())
+        flagged_total = 0
+        for h in case["heads"]:
+            qh, kh, vh = f64(q13[0, h]), f64(k13[0, h]), f64(v13[0, h])
+            sup_rows = [np.array([0])] * w.nq
+            for qb in qbs:
+                sup, flags = oracle_union_row([orc[(h, t, qb)][:qb + 1] for t in (9, 10, 11, 12)], eta)
+                got = rows[h * w.nq + qb]
+                diff = set(got.tolist()) ^ set(sup.tolist())
+                assert diff <= flags, f"{name} eta {eta} head {h} block {qb}: unflagged mismatch {diff - flags}"
+                flagged_total += len(diff)
+                if diff:
+                    continue
+                sup_rows[qb] = sup
+                ro, rl = O.sparse_attention(qh, kh, vh, sup_rows, qblocks=(qb, qb + 1))
+                sl = slice(32 * qb, 32 * qb + 32)
+                assert_attn_close(f64(o[0, h, sl]), ro, w.dtype, f"{name} eta {eta} head {h} block {qb} O")
+                assert_lse_close(f64(lse[0, h, sl]), rl, w.dtype, f"{name} eta {eta} head {h} block {qb}")
+        note(f"{name} eta={eta}: flagged mismatching blocks {flagged_total}")
+
+
+@pytest.mark.parametrize("name", ["4k", "16k"])
+def test_fullsize_dense_rows(name):
+    from block_sparse_attention_wise_amd import wise
+    w = WORKLOADS[name]
+    case = CASES[name]
+    g = Generator(w)
+    (q, k, v), dev = step_pair(g, 1)
+    note(f"{name} dense step 1")
+    o, lse = wise.dense_attn(*dev, want_lse=True)
+    torch.cuda.synchronize()
+    qbs = case["qblocks"] if case["qblocks"] is not None else [0, 1, w.nq // 2, w.nq - 1]
+    for h in case["heads"]:
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        for qb in qbs:
+            ro, rl = O.causal_attention(qh, kh, vh, rows=(32 * qb, 32 * qb + 32))
+            sl = slice(32 * qb, 32 * qb + 32)
+            assert_attn_close(f64(o[0, h, sl]), ro, w.dtype, f"{name} head {h} block {qb} O")
+            assert_lse_close(f64(lse[0, h, sl]), rl, w.dtype, f"{name} head {h} block {qb}")

@@ -11,7 +11,7 @@ import torch
 import oracle as O
 from block_sparse_attention_wise_amd.synthetic import WORKLOADS, Generator
 from parity_helpers import (assert_attn_close, assert_lse_close, assert_mass_close, compare_supports,
-                            csr_rows, f64, note, oracle_union_row, schedule_from_rows)
+                            csr_rows, f64, note, oracle_union_row, schedule_from_rows, step_pair)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -35,9 +35,9 @@ def _gen(name):
 @pytest.mark.parametrize("name", SMALL)
 def test_dense_attention(name):
     wise, w = _wise(), WORKLOADS[name]
-    q, k, v = _gen(name).step_torch(1, DEV)
+    (q, k, v), dev = step_pair(_gen(name), 1)
     note(f"dense {name}")
-    o, lse = wise.dense_attn(q, k, v, want_lse=True)
+    o, lse = wise.dense_attn(*dev, want_lse=True)
     torch.cuda.synchronize()
     for h in range(w.heads):
         ro, rl = O.causal_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]))
@@ -48,9 +48,9 @@ def test_dense_attention(name):
 @pytest.mark.parametrize("name", SMALL)
 def test_discovery_attention_and_block_mass(name):
     wise, w = _wise(), WORKLOADS[name]
-    q, k, v = _gen(name).step_torch(9, DEV)
+    (q, k, v), dev = step_pair(_gen(name), 9)
     note(f"mass {name}")
-    o, lse, mass = wise.full_attn_mass(q, k, v, want_lse=True, want_mass=True)
+    o, lse, mass = wise.full_attn_mass(*dev, want_lse=True, want_mass=True)
     torch.cuda.synchronize()
     for h in range(w.heads):
         qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
@@ -127,9 +127,9 @@ def test_sparse_attention_on_oracle_schedule(name):
         rows += O.union_supports(per_step)
     sched = schedule_from_rows(rows, DEV)
     for t in (13, 32):
-        q, k, v = _gen(name).step_torch(t, DEV)
+        (q, k, v), dev = step_pair(_gen(name), t)
         note(f"sparse {name} step {t}")
-        o, lse = wise.sparse_attn(q, k, v, sched, want_lse=True)
+        o, lse = wise.sparse_attn(*dev, sched, want_lse=True)
         torch.cuda.synchronize()
         for h in range(w.heads):
             ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), rows[h * w.nq:(h + 1) * w.nq])
@@ -162,9 +162,9 @@ def test_end_to_end_trajectory(name):
     note(f"e2e {name}: flagged mismatching blocks {flagged}")
     assert not bad, f"{len(bad)} rows differ outside flagged blocks, first {bad[:3]}"
     same = [r for r in range(len(ref_rows)) if np.array_equal(gpu_rows[r], ref_rows[r])]
-    q, k, v = g.step_torch(20, DEV)
+    (q, k, v), dev = step_pair(g, 20)
     note(f"e2e {name} sparse step 20")
-    o, lse = wise.sparse_attn(q, k, v, sched, want_lse=True)
+    o, lse = wise.sparse_attn(*dev, sched, want_lse=True)
     torch.cuda.synchronize()
     for h in range(w.heads):
         ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), ref_rows[h * w.nq:(h + 1) * w.nq])
@@ -187,9 +187,9 @@ def test_eta_one_sparse_equals_dense(name):
     note(f"eta=1 {name}")
     sched = wise.build_support(mass, 1.0)
     assert int(sched.nnz.item()) == w.heads * w.nq * (w.nq + 1) // 2
-    q, k, v = g.step_torch(13, DEV)
-    os_, ls = wise.sparse_attn(q, k, v, sched, want_lse=True)
-    od, ld = wise.dense_attn(q, k, v, want_lse=True)
+    (q, k, v), dev = step_pair(g, 13)
+    os_, ls = wise.sparse_attn(*dev, sched, want_lse=True)
+    od, ld = wise.dense_attn(*dev, want_lse=True)
     torch.cuda.synchronize()
     # same blocks in the same order; only instruction scheduling may differ
     assert_attn_close(f64(os_), f64(od), w.dtype, "sparse(eta=1) vs dense")

@@ -1,0 +1,74 @@
+"""Host-side logic: the seeded input generator and bench.py's bookkeeping (CPU)."""
+import json
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle as O
+from block_sparse_attention_wise_amd import synthetic as S
+
+
+def test_generator_is_deterministic_and_head_local():
+    w = S.WORKLOADS["1k"]
+    a = S.Generator(w, heads=[0, 3]).step_f32(9)
+    b = S.Generator(w, heads=[3]).step_f32(9)
+    for x, y in zip(a, b):
+        assert x.shape == (2, 1024, 128)
+        np.testing.assert_array_equal(x[1], y[0])       # a head does not depend on the others
+    c = S.Generator(w, heads=[0, 3]).step_f32(9)
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_drift_shrinks_with_step_and_steps_differ():
+    w = S.WORKLOADS["tiny"]
+    g = S.Generator(w)
+    base = g.base[0]
+    d1 = np.abs(g.step_f32(1)[0][0] - base[0]).std()
+    d32 = np.abs(g.step_f32(32)[0][0] - base[0]).std()
+    assert 0.02 < d1 < 0.08 and d32 < d1 / 10
+    with pytest.raises(ValueError):
+        g.step_f32(0)
+
+
+def test_torch_cast_matches_dtype():
+    import torch
+    q, k, v = S.Generator(S.WORKLOADS["1k"], heads=[0]).step_torch(5)
+    assert q.dtype == torch.bfloat16 and q.shape == (1, 1, 1024, 128)
+    q, k, v = S.Generator(S.WORKLOADS["tiny"]).step_torch(5)
+    assert q.dtype == torch.float32 and q.shape == (1, 1, 256, 64)
+
+
+def test_planted_relevance_concentrates_attention():
+    # the scaled reading gives a sparse working set; the literal one nearly none
+    w = S.WORKLOADS["1k"]
+    dens = {}
+    for mode in ("scaled", "literal"):
+        q, k, _ = S.base_head(w, 0, planted=mode)
+        r = O.block_mass(q, k)
+        rows = O.step_supports(r, 0.95)
+        dens[mode] = O.block_density(rows, w.nq)
+    assert dens["scaled"] < 0.6 < dens["literal"]
+
+
+def test_pairs_from_csr_matches_oracle():
+    rows = [np.array([0]), np.array([0, 1]), np.array([1]), np.array([0, 2, 3]), np.array([5, 9])]
+    nq = 5
+    rp, ci = O.build_csr(rows)
+    assert bench.pairs_from_csr(rp, ci, nq) == O.scheduled_pairs(rows, nq)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    out = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                         cwd=bench._ROOT)
+    assert out.returncode == 2
+    assert "one GPU" in json.loads(out.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_traffic_record_is_tied_to_the_kernel_source():
+    t = bench.measured_traffic("4k")
+    assert t is None or t > 1e8
+    assert bench.measured_traffic("16k") is None
