@@ -222,7 +222,7 @@ struct UnionList {
 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void attn_stream_kernel(AttnBf16Args a) {
+__device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   using T = Tile<D>;
   constexpr int CPT = (32 * T::C8) / 256;  // 16-byte chunks of one tile per thread
   constexpr bool SPARSE = MODE == kSparse;
@@ -381,6 +381,17 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnBf16Args a) {
   }
 }
 
+// Dense modes run 3 workgroups per CU (168 VGPRs); the sparse mode keeps 2
+// (its row bitmasks and union cursor need the extra registers).
+template <int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_dense_kernel(AttnBf16Args a) {
+  attn_stream<D, MODE>(a);
+}
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sparse_kernel(AttnBf16Args a) {
+  attn_stream<D, kSparse>(a);
+}
+
 // ------------------------------------------------------------------ launch
 
 hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream) {
@@ -388,18 +399,18 @@ hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bo
   const dim3 grid(bhn * ((a.nq + kWaves - 1) / kWaves)), block(64 * kWaves);
   if (head_dim == 128) {
     if (sparse)
-      hipLaunchKernelGGL((attn_stream_kernel<128, kSparse>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_sparse_kernel<128>), grid, block, 0, stream, a);
     else if (mass)
-      hipLaunchKernelGGL((attn_stream_kernel<128, kDenseMass>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_dense_kernel<128, kDenseMass>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_stream_kernel<128, kDense>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_dense_kernel<128, kDense>), grid, block, 0, stream, a);
   } else {
     if (sparse)
-      hipLaunchKernelGGL((attn_stream_kernel<64, kSparse>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_sparse_kernel<64>), grid, block, 0, stream, a);
     else if (mass)
-      hipLaunchKernelGGL((attn_stream_kernel<64, kDenseMass>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_dense_kernel<64, kDenseMass>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_stream_kernel<64, kDense>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_dense_kernel<64, kDense>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
