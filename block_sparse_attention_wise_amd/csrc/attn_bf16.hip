@@ -197,27 +197,57 @@ constexpr int kMaxMaskWords = 128;  // sparse rows: nq <= 4096
 
 enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2 };
 
-// Key-block lists; next() is wave-uniform (scalar) control flow.
+// Key-block lists.  next() is wave-uniform (scalar) control flow and returns an
+// entry (block << 4) | mask, bit w of mask set when wavefront w's row takes the
+// block, or -1 at the end.
 struct DenseList {
   int b, nb;
-  __device__ __forceinline__ int next() { return b < nb ? b++ : -1; }
+  __device__ __forceinline__ int next() { return b < nb ? (b++ << 4) | 0xF : -1; }
 };
+// union of the workgroup's rows, ascending, from their bitmasks in LDS
 struct UnionList {
   const uint32_t* masks;  // [kWaves][kMaxMaskWords] in LDS
   int nwords, wd;
   uint32_t u;
-  __device__ __forceinline__ uint32_t word(int w) const {
-    return __builtin_amdgcn_readfirstlane(masks[w] | masks[kMaxMaskWords + w] | masks[2 * kMaxMaskWords + w] |
-                                          masks[3 * kMaxMaskWords + w]);
+  __device__ __forceinline__ uint32_t row_word(int r, int w) const {
+    return __builtin_amdgcn_readfirstlane(masks[r * kMaxMaskWords + w]);
   }
   __device__ __forceinline__ int next() {
     while (u == 0u) {
       if (++wd >= nwords) return -1;
-      u = word(wd);
+      u = row_word(0, wd) | row_word(1, wd) | row_word(2, wd) | row_word(3, wd);
     }
     const int bit = __builtin_ctz(u);
     u &= u - 1u;
-    return 32 * wd + bit;
+    int m = 0;
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r) m |= ((row_word(r, wd) >> bit) & 1u) << r;
+    return ((32 * wd + bit) << 4) | m;
+  }
+};
+// a precomputed execution plan (wise_build_support): entries in trip order,
+// read 64 at a time, one per lane; entries naming a block past the group's last
+// query block, or with no row, are skipped
+struct PlanList {
+  const int32_t* e;
+  int base, end, qlast, lane;
+  int cur;
+  int idx;  // next entry within the current chunk
+  __device__ __forceinline__ void load_chunk() {
+    cur = base + lane < end ? e[base + lane] : -1;
+    idx = 0;
+  }
+  __device__ __forceinline__ int next() {
+    for (;;) {
+      if (idx == 64) {
+        base += 64;
+        if (base >= end) return -1;
+        load_chunk();
+      }
+      if (base + idx >= end) return -1;
+      const int v = __builtin_amdgcn_readlane(cur, idx++);
+      if (v >= 0 && (v >> 4) <= qlast && (v & 0xF) != 0) return v;
+    }
   }
 };
 
@@ -254,7 +284,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * min(qb, a.nq - 1) + i) * D, h);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-  if (SPARSE) {
+  if (SPARSE && a.plan == nullptr) {
     // this wavefront's row as a bitmask over key blocks (entries outside 0..qb
     // and offsets outside 0..col_cap are ignored; duplicates count once)
     const int nwords = (qlast >> 5) + 1;
@@ -280,7 +310,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   struct Stage {
     bf16x8 k[CPT], v[CPT];
   };
-  auto gload = [&](Stage& r, int b, bool with_v) {
+  auto gload = [&](Stage& r, int e, bool with_v) {
+    const int b = e >> 4;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = tid + 256 * u;
@@ -297,12 +328,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       if (with_v) *reinterpret_cast<bf16x8*>(&vt[buf][(c / T::C8) * T::VSTRIDE + (c % T::C8) * 8]) = r.v[u];
     }
   };
-  auto member = [&](int b) -> bool {
-    if (!SPARSE) return active && b <= qb;
-    return (__builtin_amdgcn_readfirstlane(rmask[wave * kMaxMaskWords + (b >> 5)]) >> (b & 31)) & 1u;
-  };
+  auto member = [&](int e) -> bool { return active && ((e >> wave) & 1) && (e >> 4) <= qb; };
 
-  // Runs `work(b, buf)` over the list, two blocks per trip: the trip's two
+  // Runs `work(entry, buf)` over the list, two blocks per trip: the trip's two
   // tiles sit in LDS buffers 0 and 1 while the next two are fetched into the
   // register stages; every load is waited for inside the trip it was issued in,
   // so the compiler's wait counts stay exact across the loop back-edge.
@@ -333,16 +361,25 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
 
   RowState<D> st;
   st.init();
-  auto attend = [&](int b, int buf) {
-    if (member(b)) {
+  auto attend = [&](int e, int buf) {
+    if (member(e)) {
       bf16x8 kf[T::NC];
       load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
-      attend_block<D>(st, kf, qf, vt[buf], b == qb, i, h, lane, a.scale_log2);
+      attend_block<D>(st, kf, qf, vt[buf], (e >> 4) == qb, i, h, lane, a.scale_log2);
     }
   };
-  if (SPARSE) {
+  if (SPARSE && a.plan != nullptr) {
+    const int groups = bhn * ngroups, g = bh * ngroups + grp;
+    const int64_t cap = a.plan_cap - groups - 1;  // readable entries after the offsets
+    int64_t p0 = a.plan[g], p1 = a.plan[g + 1];
+    p0 = p0 < 0 ? 0 : (p0 > cap ? cap : p0);
+    p1 = p1 < p0 ? p0 : (p1 > cap ? cap : p1);
+    PlanList list{a.plan + groups + 1, (int)p0, (int)p1, qlast, lane, -1, 64};
+    if (list.base < list.end) list.load_chunk();
+    stream(list, true, attend);
+  } else if (SPARSE) {
     UnionList list{rmask, (qlast >> 5) + 1, 0, 0u};
-    list.u = list.word(0);
+    list.u = list.row_word(0, 0) | list.row_word(1, 0) | list.row_word(2, 0) | list.row_word(3, 0);
     stream(list, true, attend);
   } else {
     DenseList list{0, qlast + 1};
@@ -360,7 +397,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     // a second sweep over the keys now that every row's log-sum-exp is final.
     float* mrow = a.mass + (size_t)(bh * a.nq + qb) * a.nq;
     DenseList list{0, qlast + 1};
-    stream(list, false, [&](int b, int buf) {
+    stream(list, false, [&](int e, int buf) {
+      const int b = e >> 4;
       if (active && b <= qb) {
         bf16x8 kf[T::NC];
         load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);

@@ -17,6 +17,8 @@ struct AttnBf16Args {
   const int32_t* row_ptr;    // sparse kernel only
   const int32_t* col_idx;    // sparse kernel only
   int64_t col_cap;           // readable col_idx entries (<= INT32_MAX)
+  const int32_t* plan;       // sparse kernel: execution plan of wise_build_support, or null
+  int64_t plan_cap;          // readable plan entries (<= INT32_MAX)
   int seqlen;
   int nq;
   int rows;                  // batch * heads * nq
@@ -42,7 +44,8 @@ struct AttnF32Args {
 hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
 size_t support_workspace_bytes(int bh, int nq);
+size_t plan_capacity(int bh, int nq);
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, void* workspace, hipStream_t stream);
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream);
 
 }  // namespace wise

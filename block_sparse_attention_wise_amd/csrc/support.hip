@@ -183,15 +183,121 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
   }
 }
 
+// ---------------------------------------------------------------- execution plan
+//
+// Groups of kPlanRows consecutive query blocks of one head are the sparse
+// kernel's work units.  A group's plan lists the union of its rows' key blocks,
+// each entry (block << 4) | membership mask (bit w: row q0 + w schedules it),
+// ordered in pairs ("trips" of two LDS tiles) so that the two tiles of a trip
+// overlap in as few rows as possible: a wavefront then rarely has two blocks to
+// process in one trip, and the trips are shorter.  The order of a row's blocks
+// only changes the floating-point summation order of its softmax.
+
+constexpr int kPlanRows = 4;
+
+// union popcount of each group -> counts[g]
+__global__ __launch_bounds__(64) void group_count_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
+                                                         int32_t* counts) {
+  const int g = blockIdx.x, lane = threadIdx.x;
+  const int bh = g / ngroups, q0 = kPlanRows * (g - bh * ngroups);
+  const int qlast = min(q0 + kPlanRows, nq) - 1;
+  const int words = (qlast >> 5) + 1;
+  int c = 0;
+  for (int w = lane; w < words; w += 64) {
+    uint32_t u = 0u;
+    for (int r = q0; r <= qlast; ++r) u |= masks[(size_t)(bh * nq + r) * nwords + w];
+    c += __popc(u);
+  }
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if (lane == 0) counts[g] = c;
+}
+
+// one wavefront per group: collect (block, mask) tiles, bucket them by mask,
+// then greedily pair each tile with a tile of a disjoint (else least
+// overlapping) mask, heaviest masks first.
+__global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
+                                                        const int32_t* plan_off, int32_t* entries) {
+  __shared__ int32_t tiles[kMaxNq];
+  __shared__ int32_t sorted_tiles[kMaxNq];
+  __shared__ int32_t bcount[16], bstart[16];
+  const int g = blockIdx.x, lane = threadIdx.x;
+  const int bh = g / ngroups, q0 = kPlanRows * (g - bh * ngroups);
+  const int qlast = min(q0 + kPlanRows, nq) - 1;
+  const int words = (qlast >> 5) + 1;
+  if (lane < 16) bcount[lane] = 0;
+  __syncthreads();
+  // ascending union tiles with their membership masks
+  int n = 0;
+  for (int w = 0; w < words; ++w) {
+    const int b = 32 * w + (lane & 31);
+    int m = 0;
+    if (lane < 32) {
+      for (int r = q0; r <= qlast; ++r)
+        if ((masks[(size_t)(bh * nq + r) * nwords + w] >> (lane & 31)) & 1u) m |= 1 << (r - q0);
+    }
+    const uint64_t present = __ballot(m != 0);
+    const int pos = n + __popcll(present & ((1ull << lane) - 1ull));
+    if (m != 0) {
+      tiles[pos] = (b << 4) | m;
+      atomicAdd(&bcount[m], 1);
+    }
+    n += __popcll(present);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    int acc = 0;
+    for (int m = 0; m < 16; ++m) {
+      bstart[m] = acc;
+      acc += bcount[m];
+      bcount[m] = 0;
+    }
+  }
+  __syncthreads();
+  for (int t = lane; t < n; t += 64) {
+    const int m = tiles[t] & 15;
+    sorted_tiles[bstart[m] + atomicAdd(&bcount[m], 1)] = tiles[t];
+  }
+  __syncthreads();
+  if (lane == 0) {
+    // masks by decreasing popcount
+    const int order[15] = {15, 14, 13, 11, 7, 12, 10, 9, 6, 5, 3, 8, 4, 2, 1};
+    int32_t* out = entries + plan_off[g];
+    int k = 0;
+    for (int oi = 0; oi < 15; ++oi) {
+      const int m = order[oi];
+      while (bcount[m] > 0) {
+        out[k++] = sorted_tiles[bstart[m] + --bcount[m]];
+        int best = -1, best_score = 1 << 30;
+        for (int p = 1; p < 16; ++p) {
+          if (bcount[p] == 0) continue;
+          // prefer disjoint masks, then the fewest shared rows, then the heaviest partner
+          const int score = 16 * __popc(p & m) - __popc(p);
+          if (score < best_score) {
+            best_score = score;
+            best = p;
+          }
+        }
+        if (best >= 0) out[k++] = sorted_tiles[bstart[best] + --bcount[best]];
+      }
+    }
+  }
+}
+
+size_t plan_capacity(int bh, int nq) {
+  const size_t groups = (size_t)bh * ((nq + kPlanRows - 1) / kPlanRows);
+  return groups + 1 + groups * (size_t)nq;
+}
+
 size_t support_workspace_bytes(int bh, int nq) {
   const size_t rows = (size_t)bh * nq;
   const size_t nwords = (nq + 31) / 32;
+  const size_t groups = (size_t)bh * ((nq + kPlanRows - 1) / kPlanRows);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al(rows * nwords * 4) + al(rows * 4);
+  return al(rows * nwords * 4) + al(rows * 4) + al(groups * 4);
 }
 
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, void* workspace, hipStream_t stream) {
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -211,6 +317,20 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.masks, nwords, row_ptr, col_idx);
+  e = hipGetLastError();
+  if (e != hipSuccess || plan == nullptr) return e;
+  // execution plan: plan[0..groups] = entry offsets, entries follow
+  const int ngroups = (nq + kPlanRows - 1) / kPlanRows;
+  const int groups = bh * ngroups;
+  int32_t* gcounts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4) + al(rows * 4));
+  hipLaunchKernelGGL(group_count_kernel, dim3(groups), dim3(64), 0, stream, a.masks, nq, nwords, ngroups, gcounts);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, gcounts, groups, plan, plan + groups);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, a.masks, nq, nwords, ngroups, plan,
+                     plan + groups + 1);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ namespace {
 
 constexpr int kBlock = 32;
 constexpr int kMaxSparseBlocks = 4096;  // bf16 sparse kernel: key blocks per row bitmask
+constexpr int kPlanRows = 4;            // query blocks per execution-plan group
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -38,15 +39,17 @@ float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.
 
 wise_status run_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, const void* q, const void* k,
                      const void* v, void* o, float* lse, float* mass, const int32_t* row_ptr,
-                     const int32_t* col_idx, int64_t col_cap, bool sparse, float scale, void* stream) {
+                     const int32_t* col_idx, int64_t col_cap, const int32_t* plan, int64_t plan_cap, bool sparse,
+                     float scale, void* stream) {
   if (col_cap > INT32_MAX) col_cap = INT32_MAX;
+  if (plan_cap > INT32_MAX) plan_cap = INT32_MAX;
   const int nq = seqlen / kBlock;
   const int rows = batch * heads * nq;
   const float sc = resolve_scale(scale, head_dim);
   hipError_t e;
   if (dt == WISE_BF16) {
     AttnBf16Args a{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                   static_cast<__bf16*>(o), lse, mass, row_ptr, col_idx, col_cap, seqlen, nq, rows,
+                   static_cast<__bf16*>(o), lse, mass, row_ptr, col_idx, col_cap, plan, plan_cap, seqlen, nq, rows,
                    sc * 1.4426950408889634f};
     e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
   } else {
@@ -82,8 +85,8 @@ wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int seqlen,
   wise_status st = check_attn_shape(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
   if (st != WISE_OK) return st;
   if (mass && !aligned4(mass)) return WISE_ERR_INVALID_ARG;
-  return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, mass, nullptr, nullptr, 0, false, scale,
-                  stream);
+  return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, mass, nullptr, nullptr, 0, nullptr, 0, false,
+                  scale, stream);
 }
 
 wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
@@ -98,9 +101,15 @@ size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps) {
   return support_workspace_bytes(bh, nq);
 }
 
+size_t wise_build_support_plan_capacity(int bh, int nq) {
+  if (bh <= 0 || nq <= 0 || nq > 4096) return 0;
+  const size_t cap = plan_capacity(bh, nq);
+  return cap > (size_t)INT32_MAX ? 0 : cap;
+}
+
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta, int32_t* row_ptr,
-                               int32_t* col_idx, int64_t col_capacity, int32_t* nnz, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               int32_t* col_idx, int64_t col_capacity, int32_t* nnz, int32_t* plan,
+                               int64_t plan_capacity, void* workspace, size_t workspace_bytes, void* stream) {
   if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
   if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
   if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
@@ -110,22 +119,31 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
   if (worst > INT32_MAX) return WISE_ERR_INVALID_ARG;
   if (col_capacity < worst) return WISE_ERR_INVALID_ARG;
   if (workspace_bytes < support_workspace_bytes(bh, nq)) return WISE_ERR_INVALID_ARG;
-  hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, row_ptr, col_idx, nnz, workspace,
+  if (plan != nullptr) {
+    const size_t need = wise_build_support_plan_capacity(bh, nq);
+    if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
+  }
+  hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, row_ptr, col_idx, nnz, plan, workspace,
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
                              const void* q, const void* k, const void* v, void* o, float* lse,
-                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity, float scale,
-                             void* stream) {
+                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                             const int32_t* plan, int64_t plan_capacity, float scale, void* stream) {
   wise_status st = check_attn_shape(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
   if (st != WISE_OK) return st;
   if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
   if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
   if (dt == WISE_BF16 && seqlen / kBlock > kMaxSparseBlocks) return WISE_ERR_UNSUPPORTED;
+  if (plan != nullptr) {
+    const int64_t groups = (int64_t)batch * heads * ((seqlen / kBlock + kPlanRows - 1) / kPlanRows);
+    if (!aligned4(plan) || plan_capacity < groups + 1) return WISE_ERR_INVALID_ARG;
+    if (dt != WISE_BF16) plan = nullptr;  // the fp32 kernel walks the CSR rows
+  }
   return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, nullptr, row_ptr, col_idx, col_capacity,
-                  true, scale, stream);
+                  plan, plan_capacity, true, scale, stream);
 }
 
 }  // extern "C"

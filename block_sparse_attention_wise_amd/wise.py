@@ -40,9 +40,12 @@ def _load():
     lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
     lib.wise_build_support.restype = i32
-    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
+    lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
+    lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
     lib.wise_sparse_attn.restype = i32
-    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, f32, vp]
+    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, f32,
+                                     vp]
     return lib
 
 
@@ -143,42 +146,62 @@ def build_support_workspace_bytes(bh: int, nq: int, num_steps: int) -> int:
     return int(lib.wise_build_support_workspace_bytes(bh, nq, num_steps))
 
 
+def build_support_plan_capacity(bh: int, nq: int) -> int:
+    return int(lib.wise_build_support_plan_capacity(bh, nq))
+
+
 class Schedule:
-    """Device-resident CSR schedule: row_ptr [rows+1], col_idx [capacity], nnz [1] (int32)."""
+    """Device-resident CSR schedule: row_ptr [rows+1], col_idx [capacity], nnz [1] (int32),
+    and optionally the execution plan of the same schedule (int32, or None)."""
 
-    def __init__(self, row_ptr, col_idx, nnz, bh, nq):
+    def __init__(self, row_ptr, col_idx, nnz, bh, nq, plan=None):
         self.row_ptr, self.col_idx, self.nnz, self.bh, self.nq = row_ptr, col_idx, nnz, bh, nq
+        self.plan = plan
 
 
-def alloc_schedule(bh: int, nq: int, device):
+def alloc_schedule(bh: int, nq: int, device, *, with_plan: bool = True):
     cap = bh * nq * (nq + 1) // 2
+    plan = None
+    if with_plan:
+        plan = torch.empty(build_support_plan_capacity(bh, nq), dtype=torch.int32, device=device)
     return Schedule(torch.empty(bh * nq + 1, dtype=torch.int32, device=device),
                     torch.empty(max(cap, 1), dtype=torch.int32, device=device),
-                    torch.empty(1, dtype=torch.int32, device=device), bh, nq)
+                    torch.empty(1, dtype=torch.int32, device=device), bh, nq, plan)
 
 
-def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspace=None, stream=None):
-    """Selection + temporal union + CSR from masses [num_steps, b*h, nq, nq] (fp32)."""
+def _plan_args(schedule: Schedule):
+    if schedule.plan is None:
+        return None, 0
+    p = schedule.plan
+    if p.dtype != torch.int32 or not p.is_contiguous():
+        raise ValueError("schedule.plan must be a contiguous int32 tensor")
+    return _ptr(p), p.numel()
+
+
+def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspace=None, stream=None,
+                  with_plan: bool = True):
+    """Selection + temporal union + CSR (+ execution plan) from masses [num_steps, b*h, nq, nq] (fp32)."""
     if mass.dim() != 4 or mass.shape[2] != mass.shape[3]:
         raise ValueError("mass must be [num_steps, batch*heads, nq, nq]")
     if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
         raise ValueError("mass must be a contiguous float32 device tensor")
     steps, bh, nq, _ = mass.shape
     if schedule is None:
-        schedule = alloc_schedule(bh, nq, mass.device)
+        schedule = alloc_schedule(bh, nq, mass.device, with_plan=with_plan)
     need = build_support_workspace_bytes(bh, nq, steps)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=mass.device)
     st = lib.wise_build_support(bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
                                 _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
-                                _ptr(workspace), workspace.numel(), _stream(stream))
+                                *_plan_args(schedule), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "wise_build_support")
     return schedule
 
 
 def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=False, scale=None,
                 block=BLOCK, stream=None):
-    """Block-sparse causal attention over a CSR schedule.  Returns (out, lse)."""
+    """Block-sparse causal attention over a CSR schedule (walking its execution plan when it
+    carries one).  Returns (out, lse)."""
     b, h, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     if want_lse and lse is None:
@@ -191,6 +214,7 @@ def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=Fal
         raise ValueError("row_ptr too short for this shape")
     st = lib.wise_sparse_attn(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                               _ptr(lse), _ptr(schedule.row_ptr), _ptr(schedule.col_idx),
-                              schedule.col_idx.numel(), float(scale or 0.0), _stream(stream))
+                              schedule.col_idx.numel(), *_plan_args(schedule), float(scale or 0.0),
+                              _stream(stream))
     _check(st, "wise_sparse_attn")
     return out, lse

@@ -49,7 +49,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 1
+#define WISE_ABI_VERSION 2
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -87,6 +87,13 @@ wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int seqlen, int
 size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
 
 /*
+ * int32 entries of the optional execution plan wise_build_support can emit
+ * beside the CSR schedule for bh rows of nq query blocks (0 on invalid sizes):
+ * G + 1 + G*nq with G = bh * ceil(nq / 4) query-block groups.
+ */
+size_t wise_build_support_plan_capacity(int bh, int nq);
+
+/*
  * Working-set schedule construction (one-time, after the discovery steps).
  *
  * For every row (bh, q) and every step t < num_steps, the admissible key blocks
@@ -105,6 +112,18 @@ size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
  *   col_idx     : int32 [col_capacity], written; ascending within a row.
  *   col_capacity: must be >= bh*nq*(nq+1)/2 (the fully dense worst case).
  *   nnz         : int32 device scalar, written with row_ptr[bh*nq].
+ *   plan        : NULL, or int32 [plan_capacity] receiving the execution plan of
+ *                 the same schedule (the execution metadata the WISE paper, App. B,
+ *                 prepares with the sparse schedule), with
+ *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq).
+ *                 Query blocks are taken in groups of 4 consecutive blocks of one
+ *                 (batch, head); group g = bh_index*ceil(nq/4) + q/4.  plan[0..G]
+ *                 are entry offsets (group g owns entries off[g] .. off[g+1]) and
+ *                 the entries follow at plan + G + 1: each is
+ *                 (key block << 4) | membership, bit w of the membership set iff
+ *                 query block 4*(g mod ceil(nq/4)) + w lists that key block.  Each
+ *                 key block of the group's union appears once, ordered so that
+ *                 consecutive pairs share as few member rows as possible.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.
@@ -112,8 +131,8 @@ size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
  */
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta,
                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                               int32_t* nnz, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               int32_t* nnz, int32_t* plan, int64_t plan_capacity,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Late-step block-sparse causal attention over a CSR schedule.
@@ -126,16 +145,24 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
  *   row_ptr, col_idx       : the schedule (as produced by wise_build_support),
  *                            rows ordered (b*heads + h)*nq + q.
  *   col_capacity           : number of readable col_idx entries.
- * Entries outside 0..q, and offsets outside 0..col_capacity, are ignored, and a
- * block listed twice counts once.  A row left with no admissible key writes
- * o = 0 and lse = -inf (wise_build_support never produces one).  The bf16 kernel
- * supports up to 4096 key blocks per head (seqlen <= 131072); beyond that it
- * returns WISE_ERR_UNSUPPORTED.
+ *   plan, plan_capacity    : NULL, or the execution plan wise_build_support wrote
+ *                            for this same schedule, plan_capacity its readable
+ *                            int32 entries (>= G + 1).  When given, the bf16
+ *                            kernel walks the plan instead of the CSR rows (same
+ *                            result up to the order of floating-point summation);
+ *                            the fp32 kernel ignores it.
+ * Entries outside 0..q, and offsets outside 0..col_capacity (0..plan_capacity),
+ * are ignored.  In the CSR a block listed twice counts once; a plan must come
+ * from wise_build_support, which lists each block of a group once.  A row left
+ * with no admissible key writes o = 0 and lse = -inf (wise_build_support never
+ * produces one).  The bf16 kernel supports up to 4096 key blocks per head
+ * (seqlen <= 131072); beyond that it returns WISE_ERR_UNSUPPORTED.
  */
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
                              int block, const void* q, const void* k, const void* v, void* o,
                              float* lse, const int32_t* row_ptr, const int32_t* col_idx,
-                             int64_t col_capacity, float scale, void* stream);
+                             int64_t col_capacity, const int32_t* plan, int64_t plan_capacity,
+                             float scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,8 +35,11 @@ def lib():
     lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
     lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
-    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
-    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, f32, vp]
+    lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
+    lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, f32,
+                                     vp]
     lib.wise_status_string.restype = ctypes.c_char_p
     lib.wise_status_string.argtypes = [i32]
     return lib
@@ -45,14 +48,15 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"wise_full_attn_mass", "wise_dense_attn", "wise_build_support",
-                          "wise_build_support_workspace_bytes", "wise_sparse_attn",
+                          "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity",
+                          "wise_sparse_attn",
                           "wise_status_string", "wise_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in wise.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 1
+    assert lib.wise_abi_version() == 2
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -85,18 +89,28 @@ def test_workspace_bytes(lib):
     f = lib.wise_build_support_workspace_bytes
     assert f(0, 8, 4) == 0 and f(1, 0, 4) == 0 and f(1, 8, 0) == 0 and f(1, 8, 65) == 0
     assert f(1, 4097, 4) == 0
-    # bitmask words per row plus one count per row, 256-byte aligned sections
+    # bitmask words per row, one count per row and one per 4-block group, 256-byte aligned sections
     def expect(bh, nq):
         al = lambda x: (x + 255) // 256 * 256
-        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4)
+        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4) + al(bh * ((nq + 3) // 4) * 4)
     for bh, nq in ((1, 8), (32, 128), (32, 512), (3, 33)):
         assert f(bh, nq, 4) == expect(bh, nq)
 
 
-def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, ws=P2, wsb=None):
+def test_plan_capacity(lib):
+    f = lib.wise_build_support_plan_capacity
+    assert f(0, 8) == 0 and f(1, 0) == 0 and f(1, 4097) == 0
+    # group offsets (G + 1) plus at most nq union blocks per group
+    for bh, nq in ((1, 8), (32, 128), (3, 33), (1, 1)):
+        g = bh * ((nq + 3) // 4)
+        assert f(bh, nq) == g + 1 + g * nq
+
+
+def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0, ws=P2,
+           wsb=None):
     cap = bh * nq * (nq + 1) // 2 if cap is None else cap
     wsb = lib.wise_build_support_workspace_bytes(bh, nq, steps) if wsb is None else wsb
-    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, ws, wsb, None)
+    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, plan, pcap, ws, wsb, None)
 
 
 def test_build_support_validation(lib):
@@ -110,6 +124,9 @@ def test_build_support_validation(lib):
         assert _build(lib, eta=eta) == INVALID, eta
     assert _build(lib, cap=2 * 8 * 9 // 2 - 1) == INVALID
     assert _build(lib, wsb=16) == INVALID
+    need = lib.wise_build_support_plan_capacity(2, 8)
+    assert _build(lib, plan=P, pcap=need - 1) == INVALID
+    assert _build(lib, plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
     # a worst case beyond int32 row offsets is rejected
     assert _build(lib, bh=1 << 20, nq=4096, cap=1 << 62, wsb=1 << 62) == INVALID
 
@@ -117,10 +134,11 @@ def test_build_support_validation(lib):
 def test_sparse_validation(lib):
     def sp(**kw):
         a = dict(dt=BF16, b=1, h=1, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, rp=P, ci=P, cap=10,
-                 scale=0.0)
+                 plan=NULL, pcap=0, scale=0.0)
         a.update(kw)
         return lib.wise_sparse_attn(a["dt"], a["b"], a["h"], a["n"], a["d"], a["blk"], a["q"], a["k"], a["v"],
-                                    a["o"], a["lse"], a["rp"], a["ci"], a["cap"], a["scale"], None)
+                                    a["o"], a["lse"], a["rp"], a["ci"], a["cap"], a["plan"], a["pcap"], a["scale"],
+                                    None)
     assert sp(rp=NULL) == INVALID
     assert sp(ci=NULL) == INVALID
     assert sp(cap=-1) == INVALID
@@ -129,3 +147,5 @@ def test_sparse_validation(lib):
     assert sp(d=256) == UNSUPPORTED
     assert sp(n=32 * 4097) == UNSUPPORTED              # bf16 rows beyond 4096 key blocks
     assert sp(q=MIS) == INVALID
+    assert sp(plan=P, pcap=1) == INVALID                # fewer than G + 1 = 2 entries
+    assert sp(plan=ctypes.c_void_p(0x10002), pcap=64) == INVALID

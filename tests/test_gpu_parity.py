@@ -315,3 +315,76 @@ def test_uniform_attention_closed_form_on_gpu():
     assert_attn_close(f64(o[0, 0]), expect, "bf16", "uniform O")
     np.testing.assert_allclose(f64(lse[0, 0]), np.log(np.arange(1, n + 1)), atol=1e-5)
     assert_mass_close(f64(mass[0]), O.block_mass(np.zeros((n, d)), f64(k[0, 0])), "bf16", "uniform mass")
+
+
+def _decode_plan(plan, bh, nq):
+    """plan (host int32) -> {group: [(block, membership), ...]} in plan order."""
+    ng = (nq + 3) // 4
+    groups = bh * ng
+    off = plan[:groups + 1]
+    ent = plan[groups + 1:]
+    assert off[0] == 0 and np.all(np.diff(off) >= 0)
+    return {g: [(int(e) >> 4, int(e) & 15) for e in ent[off[g]:off[g + 1]]] for g in range(groups)}
+
+
+@pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0)])
+def test_execution_plan_lists_each_union_block_once(bh, nq, eta):
+    """The plan of each 4-block group holds exactly the union of its rows' key blocks,
+    each once, with the membership bits of the oracle's supports; the sparse kernel
+    gives the same rows through the plan as through the CSR."""
+    wise = _wise()
+    rng = np.random.default_rng(bh * 1000 + nq)
+    m = np.zeros((4, bh, nq, nq), dtype=np.float32)
+    for s in range(4):
+        for r in range(bh):
+            for qb in range(nq):
+                m[s, r, qb, :qb + 1] = rng.dirichlet(np.full(qb + 1, 0.4))
+    note(f"plan bh={bh} nq={nq} eta={eta}")
+    sched = wise.build_support(torch.from_numpy(m).to(DEV), eta)
+    torch.cuda.synchronize()
+    assert sched.plan is not None
+    plan = sched.plan.cpu().numpy()
+    gpu_rows = csr_rows(sched.row_ptr, sched.col_idx)
+    ref_rows, flags = [], []
+    for r in range(bh):
+        for qb in range(nq):
+            sup, fl = oracle_union_row([m[s, r, qb, :qb + 1].astype(np.float64) for s in range(4)], eta)
+            ref_rows.append(sup)
+            flags.append(fl)
+    bad, _ = compare_supports(gpu_rows, ref_rows, flags)
+    assert not bad
+    groups = _decode_plan(plan, bh, nq)
+    ng = (nq + 3) // 4
+    for g, ents in groups.items():
+        r0 = (g // ng) * nq + 4 * (g % ng)
+        rows = range(r0, min(r0 + 4, (g // ng + 1) * nq))
+        blocks = [b for b, _ in ents]
+        assert len(blocks) == len(set(blocks)), f"group {g} lists a block twice"
+        want = {}
+        for w_, r in enumerate(rows):
+            for b in gpu_rows[r].tolist():
+                want[b] = want.get(b, 0) | (1 << w_)
+        assert dict(ents) == want, f"group {g}"
+        for w_, r in enumerate(rows):
+            if set(gpu_rows[r].tolist()) == set(ref_rows[r].tolist()):
+                assert {b for b, mm in ents if (mm >> w_) & 1} == set(ref_rows[r].tolist())
+    # sparse attention through the plan vs through the CSR rows vs the oracle
+    n, d = 32 * nq, 128
+    q, k, v = (torch.from_numpy(rng.standard_normal((1, bh, n, d)).astype(np.float32)).to(torch.bfloat16)
+               for _ in range(3))
+    dq, dk, dv = q.to(DEV), k.to(DEV), v.to(DEV)
+    op, lp = wise.sparse_attn(dq, dk, dv, sched, want_lse=True)
+    csr_only = wise.Schedule(sched.row_ptr, sched.col_idx, sched.nnz, bh, nq)
+    oc, lc = wise.sparse_attn(dq, dk, dv, csr_only, want_lse=True)
+    torch.cuda.synchronize()
+    assert_attn_close(f64(op), f64(oc), "bf16", "plan vs CSR O")
+    assert float((lp - lc).abs().max()) <= 1e-5
+    for h in range(bh):
+        rows_h = ref_rows[h * nq:(h + 1) * nq]
+        ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), rows_h)
+        keep = np.zeros(n, dtype=bool)
+        for qb in range(nq):
+            if set(gpu_rows[h * nq + qb].tolist()) == set(rows_h[qb].tolist()):
+                keep[32 * qb:32 * qb + 32] = True
+        assert_attn_close(f64(op[0, h])[keep], ro[keep], "bf16", f"plan head {h} O")
+        assert_lse_close(f64(lp[0, h])[keep], rl[keep], "bf16", f"plan head {h}")
