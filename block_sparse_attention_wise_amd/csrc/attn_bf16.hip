@@ -1,30 +1,29 @@
 // bf16 causal attention kernels for gfx950: dense (discovery steps, optionally
-// with the block-mass epilogue) and block-sparse over a CSR schedule (reuse
-// steps).  Both share one per-wavefront key-block step.
+// with the block-mass epilogue) and block-sparse over a CSR schedule or its
+// execution plan (reuse steps).  Both share one per-wavefront softmax step.
 //
 // The WISE paper (Wan & Chen, arXiv 2609.27373): attention of §3, block mass of
-// §5.1 (Eq. 5), reuse mask of §5.2, CSR schedule of App. B.
+// §5.1 (Eq. 5), reuse mask of §5.2, CSR schedule and its execution metadata of
+// App. B.
 //
-// Per-wavefront step (one 32-query block against one 32-key block):
-//   S^T = K Q^T        NC x v_mfma_f32_32x32x16_bf16; S^T keeps one query per
-//                      lane (lane % 32) and 16 of the 32 keys, so the row max is
-//                      an in-lane max plus one permlane32 swap;
+// Per-wavefront step (one 32-query block against one or two 32-key blocks):
+//   S^T = K Q^T        NC x v_mfma_f32_32x32x16_bf16 per block; S^T keeps one
+//                      query per lane (lane % 32) and 16 of the 32 keys, so the
+//                      row max is an in-lane max plus one permlane32 swap;
 //   online softmax     fp32, exp2 with scale*log2(e) folded into one FMA; causal
 //                      mask only on the diagonal block; the O rescale runs only
-//                      when some row's running max moved;
+//                      when some row's running max moved by more than a slack;
 //   O^T += V^T P^T     P^T is already the MFMA B-operand layout (no data
 //                      movement); V^T comes from the V tile in LDS through
 //                      ds_read_b64_tr_b16 transposing reads.
 // The contraction index d is permuted identically for Q and K so that each lane
 // reads one contiguous half row (64 elements at d = 128).
 //
-// Dense kernel: a 4-wavefront workgroup owns 4 consecutive query blocks of one
-// head and streams key blocks 0..q through double-buffered LDS tiles shared by
-// its wavefronts (one global read of K/V per 128 queries).
-// Sparse kernel: one wavefront owns one (head, query block) row and walks its
-// scheduled key blocks; rows do not share key blocks, so K is read straight into
-// the MFMA operand registers and V staged through a private LDS tile, both
-// prefetched one block ahead.
+// Both kernels: a 4-wavefront workgroup owns 4 consecutive query blocks of one
+// head and streams a list of key blocks through LDS tiles shared by its
+// wavefronts (dense: 0..q, two tiles per trip; sparse: the union of the four
+// rows' scheduled blocks, four tiles per trip), each wavefront attending to the
+// blocks of its own row.
 #include "common.h"
 #include "kernels.h"
 
@@ -104,20 +103,48 @@ struct RowState {
 
 constexpr float kSlack = 8.f;  // log2 units
 
-// One key block: scores, causal mask on the diagonal block, online softmax, P V.
-template <int D, class QS>
-__device__ __forceinline__ void attend_block(RowState<D>& st, const bf16x8 (&kf)[Tile<D>::NC], const QS& qf,
-                                             const __bf16* vt, bool diag, int i, int h, int lane, float sl2) {
-  floatx16 s = qk_tile<D>(kf, qf);
-  if (diag) {
+// N key blocks in one online-softmax step (N = 1 or 2): scores, causal mask on
+// the diagonal block, one running-max update for all N blocks, P V.  Two blocks
+// per step give the wavefront two independent MFMA chains and twice the
+// softmax work between dependent instructions, and halve the max/rescale work
+// per block.  The K fragments are read from the LDS tiles kt[n] (row i, this
+// lane's half), the V^T operands from vt[n].
+template <int D, int N, class QS>
+__device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* const (&kt)[N], const QS& qf,
+                                             const __bf16* const (&vt)[N], const bool (&diag)[N], int i, int h,
+                                             int lane, float sl2) {
+  using T = Tile<D>;
+  floatx16 s[N];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (acc_row(r, h) > i) s[r] = -INFINITY;
+  for (int n = 0; n < N; ++n) s[n] = floatx16{};
+  // The MFMA phases run at raised wave priority, the softmax at normal: the
+  // SIMD's other wavefront then fills the matrix-core phases with its VALU work.
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(kt[n] + i * T::KSTRIDE + h * T::HALF + 8 * c);
+      s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf.get(c), s[n], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    if (diag[n]) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (acc_row(r, h) > i) s[n][r] = -INFINITY;
+    }
   }
   // pairwise trees keep the dependent-instruction chains short
   float mx[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) mx[r] = fmaxf(s[r], s[r + 8]);
+  for (int r = 0; r < 8; ++r) mx[r] = fmaxf(s[0][r], s[0][r + 8]);
+#pragma unroll
+  for (int n = 1; n < N; ++n)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) mx[r] = fmaxf(mx[r], fmaxf(s[n][r], s[n][r + 8]));
 #pragma unroll
   for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], mx[r + 4]);
   float tmax = fmaxf(fmaxf(mx[0], mx[2]), fmaxf(mx[1], mx[3]));
@@ -130,29 +157,40 @@ __device__ __forceinline__ void attend_block(RowState<D>& st, const bf16x8 (&kf)
     const float alpha = fast_exp2(st.m - m_new);
     st.l *= alpha;
 #pragma unroll
-    for (int t = 0; t < Tile<D>::NT; ++t) st.acc[t] *= alpha;
+    for (int t = 0; t < T::NT; ++t) st.acc[t] *= alpha;
     st.m = m_new;
   }
   const float m_use = st.m;
-  float pv[16];
-  bf16x8 pb[2];
+  float pv[N][16];
+  bf16x8 pb[N][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    pv[r] = fast_exp2(fmaf(s[r], sl2, -m_use));
-    pb[r >> 3][r & 7] = (__bf16)pv[r];
-  }
+  for (int n = 0; n < N; ++n)
 #pragma unroll
-  for (int r = 0; r < 8; ++r) pv[r] += pv[r + 8];
+    for (int r = 0; r < 16; ++r) {
+      pv[n][r] = fast_exp2(fmaf(s[n][r], sl2, -m_use));
+      pb[n][r >> 3][r & 7] = (__bf16)pv[n][r];
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pv[r] += pv[r + 4];
-  const float psum = (pv[0] + pv[2]) + (pv[1] + pv[3]);
+  for (int n = 1; n < N; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[0][r] += pv[n][r];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pv[0][r] += pv[0][r + 8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pv[0][r] += pv[0][r + 4];
+  const float psum = (pv[0][0] + pv[0][2]) + (pv[0][1] + pv[0][3]);
   st.l += psum;
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-  for (int t = 0; t < Tile<D>::NT; ++t) {
+  for (int t = 0; t < T::NT; ++t) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
-      st.acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt, t, c2, lane), pb[c2], st.acc[t], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+        st.acc[t] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], t, c2, lane), pb[n][c2], st.acc[t], 0, 0, 0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Normalise and store O (bf16) and the natural-log LSE of one query block.
@@ -178,51 +216,61 @@ __device__ __forceinline__ float finish_rows(const RowState<D>& st, __bf16* orow
 
 // ------------------------------------------------------------------ streaming kernel
 //
-// One 4-wavefront workgroup owns 4 consecutive query blocks q0..q0+3 of one
+// One W-wavefront workgroup owns W consecutive query blocks q0..q0+W-1 of one
 // (batch, head); wavefront w owns query block q0 + w.  The workgroup streams a
-// list of key blocks through double-buffered LDS tiles shared by its
-// wavefronts, and every wavefront runs the key-block step on the blocks of its
-// own row:
-//   dense   list = 0 .. q0+3, wavefront w takes b <= q0 + w;
-//   sparse  list = union of the 4 rows' scheduled blocks (ascending), wavefront
-//           w takes the blocks of its own CSR row.
+// list of key blocks through LDS tiles shared by its wavefronts, TRIP tiles per
+// trip, and every wavefront runs the key-block step on the blocks of its own row:
+//   dense   (W = 4, TRIP = 2) list = 0 .. q0+3, wavefront w takes b <= q0 + w;
+//   sparse  (W = 4, TRIP = 4) list = union of the 4 rows' scheduled blocks (the
+//           execution plan's order, else ascending), wavefront w takes the
+//           blocks of its own row.
 // Neighbouring query blocks share key blocks (the sink, recent context), so the
-// sparse union reads each shared block once per workgroup.  Global loads run two
-// blocks ahead of the compute through two register staging sets.
+// sparse union reads each shared block once per workgroup.  Global loads run one
+// trip ahead of the compute through register staging sets.
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;       // dense workgroups
+constexpr int kSparseWaves = kPlanRows;  // sparse workgroups
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left free
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 constexpr int kMaxMaskWords = 128;  // sparse rows: nq <= 4096
+constexpr int kEntryShift = 8;      // list entries: (block << 8) | row mask
 
 enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2 };
+constexpr int kSparseTrip = kPlanTrip;  // tiles per trip of the sparse kernel
 
 // Key-block lists.  next() is wave-uniform (scalar) control flow and returns an
-// entry (block << 4) | mask, bit w of mask set when wavefront w's row takes the
+// entry (block << 8) | mask, bit w of mask set when wavefront w's row takes the
 // block, or -1 at the end.
 struct DenseList {
   int b, nb;
-  __device__ __forceinline__ int next() { return b < nb ? (b++ << 4) | 0xF : -1; }
+  __device__ __forceinline__ int next() { return b < nb ? (b++ << kEntryShift) | 0xFF : -1; }
 };
-// union of the workgroup's rows, ascending, from their bitmasks in LDS
+// union of the workgroup's W rows, ascending, from their bitmasks in LDS
+template <int W>
 struct UnionList {
-  const uint32_t* masks;  // [kWaves][kMaxMaskWords] in LDS
+  const uint32_t* masks;  // [W][kMaxMaskWords] in LDS
   int nwords, wd;
   uint32_t u;
   __device__ __forceinline__ uint32_t row_word(int r, int w) const {
     return __builtin_amdgcn_readfirstlane(masks[r * kMaxMaskWords + w]);
   }
+  __device__ __forceinline__ uint32_t word_union(int w) const {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int r = 0; r < W; ++r) x |= row_word(r, w);
+    return x;
+  }
   __device__ __forceinline__ int next() {
     while (u == 0u) {
       if (++wd >= nwords) return -1;
-      u = row_word(0, wd) | row_word(1, wd) | row_word(2, wd) | row_word(3, wd);
+      u = word_union(wd);
     }
     const int bit = __builtin_ctz(u);
     u &= u - 1u;
     int m = 0;
 #pragma unroll
-    for (int r = 0; r < kWaves; ++r) m |= ((row_word(r, wd) >> bit) & 1u) << r;
-    return ((32 * wd + bit) << 4) | m;
+    for (int r = 0; r < W; ++r) m |= ((row_word(r, wd) >> bit) & 1u) << r;
+    return ((32 * wd + bit) << kEntryShift) | m;
   }
 };
 // a precomputed execution plan (wise_build_support): entries in trip order,
@@ -246,7 +294,7 @@ struct PlanList {
       }
       if (base + idx >= end) return -1;
       const int v = __builtin_amdgcn_readlane(cur, idx++);
-      if (v >= 0 && (v >> 4) <= qlast && (v & 0xF) != 0) return v;
+      if (v >= 0 && (v >> kEntryShift) <= qlast && (v & 0xFF) != 0) return v;
     }
   }
 };
@@ -254,25 +302,33 @@ struct PlanList {
 template <int D, int MODE>
 __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   using T = Tile<D>;
-  constexpr int CPT = (32 * T::C8) / 256;  // 16-byte chunks of one tile per thread
   constexpr bool SPARSE = MODE == kSparse;
-  __shared__ __attribute__((aligned(16))) __bf16 kt[2][32 * T::KSTRIDE];
-  __shared__ __attribute__((aligned(16))) __bf16 vt[2][32 * T::VSTRIDE];
-  __shared__ uint32_t rmask[SPARSE ? kWaves * kMaxMaskWords : 1];
+  constexpr int W = SPARSE ? kSparseWaves : kWaves;  // wavefronts = query blocks per workgroup
+  constexpr int NTHR = 64 * W;
+  constexpr int CHUNKS = 32 * T::C8;                // 16-byte chunks of one tile
+  constexpr int CPT = (CHUNKS + NTHR - 1) / NTHR;  // ... per thread
+  static_assert(CPT * NTHR == CHUNKS || CPT == 1, "tile chunks per thread");
+  // tiles per trip: the sparse lists are short and scattered, so their trips are
+  // longer (fewer barriers, more loads in flight)
+  constexpr int TRIP = SPARSE ? kSparseTrip : 2;
+
+  __shared__ __attribute__((aligned(16))) __bf16 kt[TRIP][32 * T::KSTRIDE];
+  __shared__ __attribute__((aligned(16))) __bf16 vt[TRIP][32 * T::VSTRIDE];
+  __shared__ uint32_t rmask[SPARSE ? W * kMaxMaskWords : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 31, h = lane >> 5;
-  const int ngroups = (a.nq + kWaves - 1) / kWaves;
+  const int ngroups = (a.nq + W - 1) / W;
   const int bhn = a.rows / a.nq;
   // Longest-first order over all heads: workgroup p takes the (p / bhn)-th longest
   // query group of head p % bhn.  Consecutive workgroups land on different XCDs,
   // so each XCD sees the heads congruent to it modulo 8 (bhn a multiple of 8).
   const int bh = blockIdx.x % bhn;
   const int grp = ngroups - 1 - (int)(blockIdx.x / bhn);
-  const int q0 = kWaves * grp;
+  const int q0 = W * grp;
   const int qb = q0 + wave;
   const bool active = qb < a.nq;
-  const int qlast = min(q0 + kWaves, a.nq) - 1;
+  const int qlast = min(q0 + W, a.nq) - 1;
   const size_t head_off = (size_t)bh * a.seqlen * D;
   const __bf16* kh = a.k + head_off;
   const __bf16* vh = a.v + head_off;
@@ -306,66 +362,95 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     __syncthreads();
   }
 
-  // cooperative tile copy: chunk c = tid + 256*u -> row c / C8, column chunk c % C8
+  // cooperative tile copy: chunk c = tid + NTHR*u -> row c / C8, column chunk c % C8
   struct Stage {
     bf16x8 k[CPT], v[CPT];
   };
   auto gload = [&](Stage& r, int e, bool with_v) {
-    const int b = e >> 4;
+    const int b = e >> kEntryShift;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u;
-      const size_t off = (size_t)(32 * b + c / T::C8) * D + (c % T::C8) * 8;
-      r.k[u] = *reinterpret_cast<const bf16x8*>(kh + off);
-      if (with_v) r.v[u] = *reinterpret_cast<const bf16x8*>(vh + off);
+      const int c = tid + NTHR * u;
+      if (CHUNKS % NTHR == 0 || c < CHUNKS) {
+        const size_t off = (size_t)(32 * b + c / T::C8) * D + (c % T::C8) * 8;
+        r.k[u] = *reinterpret_cast<const bf16x8*>(kh + off);
+        if (with_v) r.v[u] = *reinterpret_cast<const bf16x8*>(vh + off);
+      }
     }
   };
   auto lstore = [&](const Stage& r, int buf, bool with_v) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u;
-      *reinterpret_cast<bf16x8*>(&kt[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = r.k[u];
-      if (with_v) *reinterpret_cast<bf16x8*>(&vt[buf][(c / T::C8) * T::VSTRIDE + (c % T::C8) * 8]) = r.v[u];
+      const int c = tid + NTHR * u;
+      if (CHUNKS % NTHR == 0 || c < CHUNKS) {
+        *reinterpret_cast<bf16x8*>(&kt[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = r.k[u];
+        if (with_v) *reinterpret_cast<bf16x8*>(&vt[buf][(c / T::C8) * T::VSTRIDE + (c % T::C8) * 8]) = r.v[u];
+      }
     }
   };
-  auto member = [&](int e) -> bool { return active && ((e >> wave) & 1) && (e >> 4) <= qb; };
+  auto member = [&](int e) -> bool { return active && ((e >> wave) & 1) && (e >> kEntryShift) <= qb; };
 
-  // Runs `work(entry, buf)` over the list, two blocks per trip: the trip's two
-  // tiles sit in LDS buffers 0 and 1 while the next two are fetched into the
-  // register stages; every load is waited for inside the trip it was issued in,
-  // so the compiler's wait counts stay exact across the loop back-edge.
+  // Runs `work(entries)` over the list, TRIP blocks per trip: the trip's
+  // tiles sit in LDS buffers 0..TRIP-1 while the next trip's are fetched into
+  // the register stages; every load is waited for inside the trip it was issued
+  // in, so the compiler's wait counts stay exact across the loop back-edge.
   auto stream = [&](auto& list, bool with_v, auto&& work) {
-    Stage ra, rb;
-    int c0 = list.next();
-    int c1 = c0 >= 0 ? list.next() : -1;
-    if (c0 >= 0) gload(ra, c0, with_v);
-    if (c1 >= 0) gload(rb, c1, with_v);
-    if (c0 >= 0) lstore(ra, 0, with_v);
-    if (c1 >= 0) lstore(rb, 1, with_v);
+    Stage r[TRIP];
+    int c[TRIP];
+#pragma unroll
+    for (int u = 0; u < TRIP; ++u) c[u] = (u == 0 || c[u - 1] >= 0) ? list.next() : -1;
+#pragma unroll
+    for (int u = 0; u < TRIP; ++u)
+      if (c[u] >= 0) gload(r[u], c[u], with_v);
+#pragma unroll
+    for (int u = 0; u < TRIP; ++u)
+      if (c[u] >= 0) lstore(r[u], u, with_v);
     __syncthreads();
-    while (c0 >= 0) {
-      const int n0 = c1 >= 0 ? list.next() : -1;
-      const int n1 = n0 >= 0 ? list.next() : -1;
-      if (n0 >= 0) gload(ra, n0, with_v);
-      if (n1 >= 0) gload(rb, n1, with_v);
-      work(c0, 0);
-      if (c1 >= 0) work(c1, 1);
+    while (c[0] >= 0) {
+      int n[TRIP];
+#pragma unroll
+      for (int u = 0; u < TRIP; ++u) n[u] = (u == 0 ? c[TRIP - 1] >= 0 : n[u - 1] >= 0) ? list.next() : -1;
+#pragma unroll
+      for (int u = 0; u < TRIP; ++u)
+        if (n[u] >= 0) gload(r[u], n[u], with_v);
+      work(c);
       __syncthreads();
-      if (n0 >= 0) lstore(ra, 0, with_v);
-      if (n1 >= 0) lstore(rb, 1, with_v);
+#pragma unroll
+      for (int u = 0; u < TRIP; ++u)
+        if (n[u] >= 0) lstore(r[u], u, with_v);
       __syncthreads();
-      c0 = n0;
-      c1 = n1;
+#pragma unroll
+      for (int u = 0; u < TRIP; ++u) c[u] = n[u];
     }
   };
 
   RowState<D> st;
   st.init();
-  auto attend = [&](int e, int buf) {
-    if (member(e)) {
-      bf16x8 kf[T::NC];
-      load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
-      attend_block<D>(st, kf, qf, vt[buf], (e >> 4) == qb, i, h, lane, a.scale_log2);
+  // a trip's tiles of this wavefront's row, two per softmax step
+  auto attend = [&](const int (&c)[TRIP]) {
+    int mine = 0, dg = 0;
+#pragma unroll
+    for (int u = 0; u < TRIP; ++u) {
+      if (c[u] >= 0 && member(c[u])) mine |= 1 << u;
+      if ((c[u] >> kEntryShift) == qb) dg |= 1 << u;
+    }
+    while (__builtin_popcount(mine) >= 2) {
+      const int u0 = __builtin_ctz(mine);
+      mine &= mine - 1;
+      const int u1 = __builtin_ctz(mine);
+      mine &= mine - 1;
+      const __bf16* const kp[2] = {kt[u0], kt[u1]};
+      const __bf16* const vp[2] = {vt[u0], vt[u1]};
+      const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
+      attend_tiles<D, 2>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2);
+    }
+    while (mine) {
+      const int u0 = __builtin_ctz(mine);
+      mine &= mine - 1;
+      const __bf16* const kp[1] = {kt[u0]};
+      const __bf16* const vp[1] = {vt[u0]};
+      const bool dp[1] = {((dg >> u0) & 1) != 0};
+      attend_tiles<D, 1>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2);
     }
   };
   if (SPARSE && a.plan != nullptr) {
@@ -378,8 +463,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     if (list.base < list.end) list.load_chunk();
     stream(list, true, attend);
   } else if (SPARSE) {
-    UnionList list{rmask, (qlast >> 5) + 1, 0, 0u};
-    list.u = list.row_word(0, 0) | list.row_word(1, 0) | list.row_word(2, 0) | list.row_word(3, 0);
+    UnionList<W> list{rmask, (qlast >> 5) + 1, 0, 0u};
+    list.u = list.word_union(0);
     stream(list, true, attend);
   } else {
     DenseList list{0, qlast + 1};
@@ -397,9 +482,11 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     // a second sweep over the keys now that every row's log-sum-exp is final.
     float* mrow = a.mass + (size_t)(bh * a.nq + qb) * a.nq;
     DenseList list{0, qlast + 1};
-    stream(list, false, [&](int e, int buf) {
-      const int b = e >> 4;
-      if (active && b <= qb) {
+    stream(list, false, [&](const int (&c)[TRIP]) {
+#pragma unroll
+      for (int buf = 0; buf < TRIP; ++buf) {
+        const int b = c[buf] >> kEntryShift;
+        if (c[buf] < 0 || !active || b > qb) continue;
         bf16x8 kf[T::NC];
         load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
         floatx16 s = qk_tile<D>(kf, qf);
@@ -419,14 +506,17 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   }
 }
 
-// Dense modes run 3 workgroups per CU (168 VGPRs); the sparse mode keeps 2
-// (its row bitmasks and union cursor need the extra registers).
+// Two workgroups per CU (two wavefronts per SIMD, up to 256 VGPRs each): the
+// two-block softmax steps need the registers, and the sparse mode's four
+// register staging sets and LDS tiles per trip too.
 template <int D, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_dense_kernel(AttnBf16Args a) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_dense_kernel(
+    AttnBf16Args a) {
   attn_stream<D, MODE>(a);
 }
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sparse_kernel(AttnBf16Args a) {
+__global__ __launch_bounds__(64 * kSparseWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sparse_kernel(
+    AttnBf16Args a) {
   attn_stream<D, kSparse>(a);
 }
 
@@ -434,7 +524,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream) {
   const int bhn = a.rows / a.nq;
-  const dim3 grid(bhn * ((a.nq + kWaves - 1) / kWaves)), block(64 * kWaves);
+  const int w = sparse ? kSparseWaves : kWaves;
+  const dim3 grid(bhn * ((a.nq + w - 1) / w)), block(64 * w);
   if (head_dim == 128) {
     if (sparse)
       hipLaunchKernelGGL((attn_sparse_kernel<128>), grid, block, 0, stream, a);

@@ -7,6 +7,11 @@
 
 namespace wise {
 
+// The bf16 sparse kernel's workgroups own kPlanRows consecutive query blocks of
+// one head and hold kPlanTrip tiles per trip; the execution plan is built for both.
+constexpr int kPlanRows = 4;
+constexpr int kPlanTrip = 4;
+
 struct AttnBf16Args {
   const __bf16* q;
   const __bf16* k;

@@ -187,13 +187,16 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
 //
 // Groups of kPlanRows consecutive query blocks of one head are the sparse
 // kernel's work units.  A group's plan lists the union of its rows' key blocks,
-// each entry (block << 4) | membership mask (bit w: row q0 + w schedules it),
-// ordered in pairs ("trips" of two LDS tiles) so that the two tiles of a trip
-// overlap in as few rows as possible: a wavefront then rarely has two blocks to
-// process in one trip, and the trips are shorter.  The order of a row's blocks
-// only changes the floating-point summation order of its softmax.
+// each entry (block << 8) | membership mask (bit w: row q0 + w schedules it),
+// ordered in trips of kPlanTrip tiles (the tiles the kernel holds in LDS at
+// once, between two barriers) so that the rows' blocks spread evenly over the
+// trips: a trip lasts as long as its busiest row, so each trip is filled
+// greedily with the tiles that raise its busiest row the least.  The order of a
+// row's blocks only changes the floating-point summation order of its softmax.
 
-constexpr int kPlanRows = 4;
+static_assert(kPlanRows >= 1 && kPlanRows <= 8, "plan rows fit the 8-bit membership mask");
+static_assert(kPlanTrip >= 1 && kPlanTrip <= 16, "plan trip");
+constexpr int kMasks = 1 << kPlanRows;
 
 // union popcount of each group -> counts[g]
 __global__ __launch_bounds__(64) void group_count_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
@@ -212,19 +215,19 @@ __global__ __launch_bounds__(64) void group_count_kernel(const uint32_t* masks, 
   if (lane == 0) counts[g] = c;
 }
 
-// one wavefront per group: collect (block, mask) tiles, bucket them by mask,
-// then greedily pair each tile with a tile of a disjoint (else least
-// overlapping) mask, heaviest masks first.
+// one wavefront per group: collect (block, mask) tiles in ascending block order,
+// bucket them by mask (stable), then fill the trips greedily, every lane
+// scoring a quarter of the masks for each pick.
 __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
                                                         const int32_t* plan_off, int32_t* entries) {
   __shared__ int32_t tiles[kMaxNq];
   __shared__ int32_t sorted_tiles[kMaxNq];
-  __shared__ int32_t bcount[16], bstart[16];
+  __shared__ int32_t bcount[kMasks], bstart[kMasks];
   const int g = blockIdx.x, lane = threadIdx.x;
   const int bh = g / ngroups, q0 = kPlanRows * (g - bh * ngroups);
   const int qlast = min(q0 + kPlanRows, nq) - 1;
   const int words = (qlast >> 5) + 1;
-  if (lane < 16) bcount[lane] = 0;
+  for (int m = lane; m < kMasks; m += 64) bcount[m] = 0;
   __syncthreads();
   // ascending union tiles with their membership masks
   int n = 0;
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
     const uint64_t present = __ballot(m != 0);
     const int pos = n + __popcll(present & ((1ull << lane) - 1ull));
     if (m != 0) {
-      tiles[pos] = (b << 4) | m;
+      tiles[pos] = (b << 8) | m;
       atomicAdd(&bcount[m], 1);
     }
     n += __popcll(present);
@@ -246,39 +249,41 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
   __syncthreads();
   if (lane == 0) {
     int acc = 0;
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < kMasks; ++m) {
       bstart[m] = acc;
       acc += bcount[m];
       bcount[m] = 0;
     }
+    for (int t = 0; t < n; ++t) {  // stable: ascending blocks within a bucket
+      const int m = tiles[t] & (kMasks - 1);
+      sorted_tiles[bstart[m] + bcount[m]++] = tiles[t];
+    }
   }
   __syncthreads();
-  for (int t = lane; t < n; t += 64) {
-    const int m = tiles[t] & 15;
-    sorted_tiles[bstart[m] + atomicAdd(&bcount[m], 1)] = tiles[t];
-  }
-  __syncthreads();
-  if (lane == 0) {
-    // masks by decreasing popcount
-    const int order[15] = {15, 14, 13, 11, 7, 12, 10, 9, 6, 5, 3, 8, 4, 2, 1};
-    int32_t* out = entries + plan_off[g];
-    int k = 0;
-    for (int oi = 0; oi < 15; ++oi) {
-      const int m = order[oi];
-      while (bcount[m] > 0) {
-        out[k++] = sorted_tiles[bstart[m] + --bcount[m]];
-        int best = -1, best_score = 1 << 30;
-        for (int p = 1; p < 16; ++p) {
-          if (bcount[p] == 0) continue;
-          // prefer disjoint masks, then the fewest shared rows, then the heaviest partner
-          const int score = 16 * __popc(p & m) - __popc(p);
-          if (score < best_score) {
-            best_score = score;
-            best = p;
-          }
-        }
-        if (best >= 0) out[k++] = sorted_tiles[bstart[best] + --bcount[best]];
+  int32_t* out = entries + plan_off[g];
+  int load[kPlanRows];
+  for (int k = 0; k < n;) {
+#pragma unroll
+    for (int w = 0; w < kPlanRows; ++w) load[w] = 0;
+    for (int slot = 0; slot < kPlanTrip && k < n; ++slot) {
+      // the mask whose tile raises the trip's busiest row the least; ties go to
+      // the mask covering more rows (more work per trip), then the lower mask
+      int best = 0x7fffffff;
+      for (int m = 1 + lane; m < kMasks; m += 64) {
+        if (bcount[m] == 0) continue;
+        int mx = 0;
+#pragma unroll
+        for (int w = 0; w < kPlanRows; ++w) mx = max(mx, load[w] + ((m >> w) & 1));
+        const int key = ((32 * mx - __popc(m) + 32) << 8) | m;
+        best = min(best, key);
       }
+      for (int off = 32; off > 0; off >>= 1) best = min(best, __shfl_xor(best, off));
+      const int m = best & (kMasks - 1);
+      if (lane == 0) out[k] = sorted_tiles[bstart[m] + (--bcount[m])];
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kPlanRows; ++w) load[w] += (m >> w) & 1;
+      ++k;
     }
   }
 }

@@ -11,7 +11,6 @@ namespace {
 
 constexpr int kBlock = 32;
 constexpr int kMaxSparseBlocks = 4096;  // bf16 sparse kernel: key blocks per row bitmask
-constexpr int kPlanRows = 4;            // query blocks per execution-plan group
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

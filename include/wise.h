@@ -120,10 +120,11 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 (batch, head); group g = bh_index*ceil(nq/4) + q/4.  plan[0..G]
  *                 are entry offsets (group g owns entries off[g] .. off[g+1]) and
  *                 the entries follow at plan + G + 1: each is
- *                 (key block << 4) | membership, bit w of the membership set iff
+ *                 (key block << 8) | membership, bit w of the membership set iff
  *                 query block 4*(g mod ceil(nq/4)) + w lists that key block.  Each
- *                 key block of the group's union appears once, ordered so that
- *                 consecutive pairs share as few member rows as possible.
+ *                 key block of the group's union appears once, in runs of 4 (the
+ *                 tiles the kernel holds at once) that spread the member rows'
+ *                 blocks evenly.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.

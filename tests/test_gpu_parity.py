@@ -317,14 +317,14 @@ def test_uniform_attention_closed_form_on_gpu():
     assert_mass_close(f64(mass[0]), O.block_mass(np.zeros((n, d)), f64(k[0, 0])), "bf16", "uniform mass")
 
 
-def _decode_plan(plan, bh, nq):
+def _decode_plan(plan, bh, nq, rows_per_group=4):
     """plan (host int32) -> {group: [(block, membership), ...]} in plan order."""
-    ng = (nq + 3) // 4
+    ng = (nq + rows_per_group - 1) // rows_per_group
     groups = bh * ng
     off = plan[:groups + 1]
     ent = plan[groups + 1:]
     assert off[0] == 0 and np.all(np.diff(off) >= 0)
-    return {g: [(int(e) >> 4, int(e) & 15) for e in ent[off[g]:off[g + 1]]] for g in range(groups)}
+    return {g: [(int(e) >> 8, int(e) & 255) for e in ent[off[g]:off[g + 1]]] for g in range(groups)}
 
 
 @pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0)])
