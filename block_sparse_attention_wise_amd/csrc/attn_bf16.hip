@@ -103,6 +103,32 @@ struct RowState {
 
 constexpr float kSlack = 8.f;  // log2 units
 
+// Max of K values as a tree of three-input maxima (v_max3_f32), which also
+// spares the operand canonicalisation the compiler adds to two-input maxima of
+// MFMA results; the tree keeps the dependent chain short.
+template <int K>
+__device__ __forceinline__ float max_tree3(const float (&v)[K]) {
+  if constexpr (K == 1) {
+    return v[0];
+  } else if constexpr (K == 2) {
+    return fmaxf(v[0], v[1]);
+  } else {
+    constexpr int M = (K + 2) / 3;
+    float t[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+      const int a = 3 * k;
+      if (a + 2 < K)
+        t[k] = fmaxf(fmaxf(v[a], v[a + 1]), v[a + 2]);
+      else if (a + 1 < K)
+        t[k] = fmaxf(v[a], v[a + 1]);
+      else
+        t[k] = v[a];
+    }
+    return max_tree3<M>(t);
+  }
+}
+
 // N key blocks in one online-softmax step (N = 1 or 2): scores, causal mask on
 // the diagonal block, one running-max update for all N blocks, P V.  Two blocks
 // per step give the wavefront two independent MFMA chains and twice the
@@ -137,17 +163,12 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
         if (acc_row(r, h) > i) s[n][r] = -INFINITY;
     }
   }
-  // pairwise trees keep the dependent-instruction chains short
-  float mx[8];
+  float all[16 * N];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) mx[r] = fmaxf(s[0][r], s[0][r + 8]);
+  for (int n = 0; n < N; ++n)
 #pragma unroll
-  for (int n = 1; n < N; ++n)
-#pragma unroll
-    for (int r = 0; r < 8; ++r) mx[r] = fmaxf(mx[r], fmaxf(s[n][r], s[n][r + 8]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], mx[r + 4]);
-  float tmax = fmaxf(fmaxf(mx[0], mx[2]), fmaxf(mx[1], mx[3]));
+    for (int r = 0; r < 16; ++r) all[16 * n + r] = s[n][r];
+  float tmax = max_tree3<16 * N>(all);
   tmax = halves_max(tmax) * sl2;
   // Lazy rescale: the subtracted max only has to bound the exponent, so it is
   // raised (and O, l rescaled) only when some row's max exceeds it by more than
@@ -161,36 +182,31 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
     st.m = m_new;
   }
   const float m_use = st.m;
-  float pv[N][16];
-  bf16x8 pb[N][2];
+  // Block n's probabilities, then its P V products; the compiler overlaps
+  // block n's MFMAs with block n + 1's exponentials.  The row sum is taken over
+  // the fp32 probabilities (the log-sum-exp feeds the block masses).
+  float lsum[16];
 #pragma unroll
-  for (int n = 0; n < N; ++n)
+  for (int n = 0; n < N; ++n) {
+    bf16x8 pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pv[n][r] = fast_exp2(fmaf(s[n][r], sl2, -m_use));
-      pb[n][r >> 3][r & 7] = (__bf16)pv[n][r];
+      const float p = fast_exp2(fmaf(s[n][r], sl2, -m_use));
+      pb[r >> 3][r & 7] = (__bf16)p;
+      lsum[r] = n == 0 ? p : lsum[r] + p;
     }
 #pragma unroll
-  for (int n = 1; n < N; ++n)
+    for (int t = 0; t < T::NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pv[0][r] += pv[n][r];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) pv[0][r] += pv[0][r + 8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) pv[0][r] += pv[0][r + 4];
-  const float psum = (pv[0][0] + pv[0][2]) + (pv[0][1] + pv[0][3]);
-  st.l += psum;
-  __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int t = 0; t < T::NT; ++t) {
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int n = 0; n < N; ++n)
+      for (int c2 = 0; c2 < 2; ++c2)
         st.acc[t] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], t, c2, lane), pb[n][c2], st.acc[t], 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], t, c2, lane), pb[c2], st.acc[t], 0, 0, 0);
   }
-  __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) lsum[r] += lsum[r + 8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lsum[r] += lsum[r + 4];
+  st.l += (lsum[0] + lsum[2]) + (lsum[1] + lsum[3]);
 }
 
 // Normalise and store O (bf16) and the natural-log LSE of one query block.
