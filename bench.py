@@ -44,7 +44,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "hbm_traffic_attn_stream_sparse_4k.txt")
+TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "hbm_traffic_attn_sparse_4k.txt")
 KERNEL_SOURCES = ("attn_bf16.hip", "common.h", "kernels.h")
 
 
@@ -317,7 +317,7 @@ def main():
         "nnz_blocks": nnz,
         "timed_wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "wise_sparse_attn: attn_stream_kernel<128, kSparse>",
+            "kernel": "wise_sparse_attn: attn_sparse_kernel<128>",
             "bound": "mfma",
             "achieved": round(tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
