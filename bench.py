@@ -136,6 +136,49 @@ def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
     }
 
 
+def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
+    """Untimed-trajectory extras (the WISE paper, App. B): retained future mass of
+    the WISE schedule at late steps, and the intervention-control schedules
+    (Static-95, SizeMatched, MassMatched from step-1 masses): density, retained
+    future mass, build time and sparse-step time on each."""
+    import torch
+    bh, nq = w.batch * w.heads, w.nq
+    out = torch.empty_like(steps[1][0])
+    late = torch.empty((bh, nq, nq), dtype=torch.float32, device=mass.device)
+    m1 = torch.empty_like(late)
+    wise.full_attn_mass(*steps[1], out=out, mass=m1)
+    causal = bh * nq * (nq + 1) // 2
+
+    def timed(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    def retained(s, t):
+        wise.full_attn_mass(*steps[t], out=out, mass=late)
+        r = wise.retained_mass(late, s).cpu().numpy()
+        return {"mean": round(float(r.mean()), 5), "min": round(float(r.min()), 5)}
+
+    res = {"wise": {"block_density": round(int(sched.nnz.item()) / causal, 5),
+                    "retained_future_mass": {f"t{t}": retained(sched, t) for t in (13, 20, 32)}}}
+    for kind in ("static", "size_matched", "mass_matched"):
+        ctl = wise.alloc_schedule(bh, nq, mass.device)
+        build = lambda: wise.build_support_variant(kind, m1, eta=eta, reference=sched, schedule=ctl, workspace=ws)
+        build_ms = timed(build)
+        sparse_ms = timed(lambda: wise.sparse_attn(*steps[32], ctl, out=out))
+        res[{"static": "static95"}.get(kind, kind)] = {
+            "block_density": round(int(ctl.nnz.item()) / causal, 5),
+            "retained_future_mass": {"t32": retained(ctl, 32)},
+            "build_ms": round(build_ms, 4), "sparse_step_ms": round(sparse_ms, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +190,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-matched", action="store_true",
                     help="skip the full-support sparse runs (profiling: keeps one sparse launch kind)")
+    ap.add_argument("--no-diagnostics", action="store_true",
+                    help="skip the retained-mass and intervention-control diagnostics")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -249,6 +294,7 @@ def main():
     wall = time.perf_counter() - wall0
     m_rec = [] if args.no_matched else [matched_full() for _ in range(max(3, args.steps // 2))]
     torch.cuda.synchronize()
+    diagnostics = None if args.no_diagnostics else support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream)
 
     def ms(e0, e1):
         return e0.elapsed_time(e1)
@@ -316,6 +362,7 @@ def main():
         "pair_density": round(pairs / dense_pairs, 5),
         "nnz_blocks": nnz,
         "timed_wall_s": round(wall, 3),
+        "support_diagnostics": diagnostics,
         "roofline": {
             "kernel": "wise_sparse_attn: attn_sparse_kernel<128>",
             "bound": "mfma",

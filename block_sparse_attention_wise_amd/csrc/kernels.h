@@ -50,7 +50,12 @@ hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bo
 hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
 size_t support_workspace_bytes(int bh, int nq);
 size_t plan_capacity(int bh, int nq);
-hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int32_t* row_ptr,
+// kind: 0 cumulative-eta support per step, unioned over the steps; 1 SizeMatched and
+// 2 MassMatched against the reference schedule (steps == 1)
+hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
+                          const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
                           int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream);
+hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t* row_ptr, const int32_t* col_idx,
+                                int64_t cap, float* retained, hipStream_t stream);
 
 }  // namespace wise

@@ -5,14 +5,19 @@
 // §3 applied to the block masses of §5.1, the temporal union of App. B (WISE
 // configuration) and the CSR schedule of App. B (sparse-kernel implementation).
 //
-// Three kernels:
+// Kernels:
 //   select_union  one 256-thread workgroup per (batch*head, query block) row.
 //                 For every step: the q+1 admissible masses are bitonic-sorted in
 //                 LDS by the 64-bit key (mass desc, index asc); an exclusive fp64
 //                 prefix sum over the sorted masses marks block k as selected iff
 //                 the mass before it is still below eta; selected blocks are ORed
 //                 into the row's union bitmask.  Writes the bitmask and its
-//                 popcount to the workspace.
+//                 popcount to the workspace.  The same kernel builds the
+//                 intervention controls of the WISE paper (App. B, intervention
+//                 controls) from one step's masses: SizeMatched keeps the top-K
+//                 blocks, K the size of a reference row; MassMatched keeps the
+//                 smallest sorted prefix reaching the mass the reference row
+//                 retains.
 //   scan_counts   one workgroup: exclusive scan of the per-row counts -> row_ptr,
 //                 nnz.
 //   emit_csr      one wavefront per row: expands the bitmask into ascending
@@ -34,6 +39,12 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+enum SelectKind { kCumulative = 0, kSizeMatched = 1, kMassMatched = 2 };
+// MassMatched compares prefixes with the reference mass less this slack, so that
+// a reference row that is itself a sorted prefix selects exactly that prefix
+// whatever the summation order of the two fp64 sums.
+constexpr double kMassMatchSlack = 1e-9;
+
 struct SupportArgs {
   const float* mass;  // [steps][rows][nq][nq] with rows here = bh
   int bh, nq, steps;
@@ -41,6 +52,10 @@ struct SupportArgs {
   uint32_t* masks;    // [bh*nq][nwords]
   int32_t* counts;    // [bh*nq]
   int nwords;
+  int kind;                   // SelectKind; the matched kinds take steps == 1
+  const int32_t* ref_row_ptr;  // matched kinds: the reference schedule
+  const int32_t* ref_col_idx;
+  int64_t ref_cap;
 };
 
 __device__ __forceinline__ double block_exclusive_scan(double x, double* wsum, int tid) {
@@ -63,6 +78,7 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double* wsum, i
 __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a) {
   __shared__ uint64_t keys[kMaxNq];
   __shared__ uint32_t uni[kMaxNq / 32];
+  __shared__ uint32_t refm[kMaxNq / 32];
   __shared__ double wsum[kSelThreads / 64];
   __shared__ int cnt_part[kSelThreads / 64];
 
@@ -75,6 +91,21 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a
   while (n2 < n) n2 <<= 1;
 
   for (int w = tid; w < a.nwords; w += kSelThreads) uni[w] = 0u;
+  int ref_count = 0;
+  if (a.kind != kCumulative) {
+    // the reference row's admissible blocks (duplicates count once)
+    for (int w = tid; w < a.nwords; w += kSelThreads) refm[w] = 0u;
+    __syncthreads();
+    int64_t b0 = a.ref_row_ptr[row], b1 = a.ref_row_ptr[row + 1];
+    b0 = b0 < 0 ? 0 : (b0 > a.ref_cap ? a.ref_cap : b0);
+    b1 = b1 < b0 ? b0 : (b1 > a.ref_cap ? a.ref_cap : b1);
+    for (int64_t e = b0 + tid; e < b1; e += kSelThreads) {
+      const int b = a.ref_col_idx[e];
+      if (b >= 0 && b <= qb) atomicOr(&refm[b >> 5], 1u << (b & 31));
+    }
+    __syncthreads();
+    for (int w = 0; w < a.nwords; ++w) ref_count += __popc(refm[w]);
+  }
 
   for (int t = 0; t < a.steps; ++t) {
     const float* mrow = a.mass + (((size_t)t * a.bh + bh) * a.nq + qb) * (size_t)a.nq;
@@ -102,12 +133,35 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a
     const int per = (n + kSelThreads - 1) / kSelThreads;
     const int c0 = tid * per;
     const int c1 = min(n, c0 + per);
-    double local = 0.0;
-    for (int e = c0; e < c1; ++e) local += (double)from_ordered_bits((uint32_t)(keys[e] >> 32));
+    double local = 0.0, local_ref = 0.0;
+    for (int e = c0; e < c1; ++e) {
+      const double m = (double)from_ordered_bits((uint32_t)(keys[e] >> 32));
+      local += m;
+      if (a.kind == kMassMatched) {
+        const uint32_t b = 0xffffffffu - (uint32_t)(keys[e] & 0xffffffffu);
+        if ((refm[b >> 5] >> (b & 31)) & 1u) local_ref += m;
+      }
+    }
     double run = block_exclusive_scan(local, wsum, tid);
+    double thr = a.eta;
+    if (a.kind == kMassMatched) {
+      // the reference row's mass, summed in the same sorted order and chunking
+      const double ref_excl = block_exclusive_scan(local_ref, wsum, tid);
+      if (tid == kSelThreads - 1) wsum[0] = ref_excl + local_ref;
+      __syncthreads();
+      thr = wsum[0] - kMassMatchSlack;
+      __syncthreads();
+    }
     for (int e = c0; e < c1; ++e) {
       const uint64_t key = keys[e];
-      if (a.eta >= 1.0 || run < a.eta) {
+      bool take;
+      if (a.kind == kSizeMatched)
+        take = e < ref_count;
+      else if (a.kind == kMassMatched)
+        take = e == 0 || run < thr;
+      else
+        take = a.eta >= 1.0 || run < a.eta;
+      if (take) {
         const uint32_t b = 0xffffffffu - (uint32_t)(key & 0xffffffffu);
         atomicOr(&uni[b >> 5], 1u << (b & 31));
       }
@@ -301,7 +355,45 @@ size_t support_workspace_bytes(int bh, int nq) {
   return al(rows * nwords * 4) + al(rows * 4) + al(groups * 4);
 }
 
-hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int32_t* row_ptr,
+// retained[row] = sum of mass[row][b] over the row's distinct scheduled blocks
+// 0 <= b <= q, accumulated in fp64 (the retained attention mass of the WISE
+// paper, App. B and Table 1, per query block).
+__global__ __launch_bounds__(kSelThreads) void retained_mass_kernel(const float* mass, int nq, int nwords,
+                                                                    const int32_t* row_ptr, const int32_t* col_idx,
+                                                                    int64_t cap, float* retained) {
+  __shared__ uint32_t m[kMaxNq / 32];
+  __shared__ double part[kSelThreads / 64];
+  const int tid = threadIdx.x, row = blockIdx.x, qb = row % nq;
+  for (int w = tid; w < nwords; w += kSelThreads) m[w] = 0u;
+  __syncthreads();
+  int64_t b0 = row_ptr[row], b1 = row_ptr[row + 1];
+  b0 = b0 < 0 ? 0 : (b0 > cap ? cap : b0);
+  b1 = b1 < b0 ? b0 : (b1 > cap ? cap : b1);
+  for (int64_t e = b0 + tid; e < b1; e += kSelThreads) {
+    const int b = col_idx[e];
+    if (b >= 0 && b <= qb) atomicOr(&m[b >> 5], 1u << (b & 31));
+  }
+  __syncthreads();
+  const float* mrow = mass + (size_t)row * nq;
+  double local = 0.0;
+  for (int b = tid; b <= qb; b += kSelThreads)
+    if ((m[b >> 5] >> (b & 31)) & 1u) local += (double)mrow[b];
+  for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
+  if ((tid & 63) == 0) part[tid >> 6] = local;
+  __syncthreads();
+  if (tid == 0) retained[row] = (float)((part[0] + part[1]) + (part[2] + part[3]));
+}
+
+hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t* row_ptr, const int32_t* col_idx,
+                                int64_t cap, float* retained, hipStream_t stream) {
+  const size_t rows = (size_t)bh * nq;
+  hipLaunchKernelGGL(retained_mass_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, mass, nq,
+                     (nq + 31) / 32, row_ptr, col_idx, cap, retained);
+  return hipGetLastError();
+}
+
+hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
+                          const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
                           int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
@@ -315,6 +407,10 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   a.masks = static_cast<uint32_t*>(workspace);
   a.counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4));
   a.nwords = nwords;
+  a.kind = kind;
+  a.ref_row_ptr = ref_row_ptr;
+  a.ref_col_idx = ref_col_idx;
+  a.ref_cap = ref_cap;
   hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -59,6 +59,25 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_d
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
+// checks shared by the schedule builders
+wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_t* row_ptr, int32_t* col_idx,
+                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity, void* workspace,
+                        size_t workspace_bytes) {
+  if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
+  if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
+  if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
+    return WISE_ERR_INVALID_ARG;
+  const int64_t worst = (int64_t)bh * nq * (nq + 1) / 2;
+  if (worst > INT32_MAX) return WISE_ERR_INVALID_ARG;
+  if (col_capacity < worst) return WISE_ERR_INVALID_ARG;
+  if (workspace_bytes < support_workspace_bytes(bh, nq)) return WISE_ERR_INVALID_ARG;
+  if (plan != nullptr) {
+    const size_t need = wise_build_support_plan_capacity(bh, nq);
+    if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
+  }
+  return WISE_OK;
+}
+
 }  // namespace
 }  // namespace wise
 
@@ -109,21 +128,54 @@ size_t wise_build_support_plan_capacity(int bh, int nq) {
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta, int32_t* row_ptr,
                                int32_t* col_idx, int64_t col_capacity, int32_t* nnz, int32_t* plan,
                                int64_t plan_capacity, void* workspace, size_t workspace_bytes, void* stream) {
-  if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
-  if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
-  if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
-    return WISE_ERR_INVALID_ARG;
+  wise_status st = check_build(bh, nq, num_steps, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
+                               workspace, workspace_bytes);
+  if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
-  const int64_t worst = (int64_t)bh * nq * (nq + 1) / 2;
-  if (worst > INT32_MAX) return WISE_ERR_INVALID_ARG;
-  if (col_capacity < worst) return WISE_ERR_INVALID_ARG;
-  if (workspace_bytes < support_workspace_bytes(bh, nq)) return WISE_ERR_INVALID_ARG;
-  if (plan != nullptr) {
-    const size_t need = wise_build_support_plan_capacity(bh, nq);
-    if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
+  hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, 0, nullptr, nullptr, 0, row_ptr, col_idx, nnz,
+                                plan, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
+}
+
+wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq, const float* mass, float eta,
+                                       const int32_t* ref_row_ptr, const int32_t* ref_col_idx,
+                                       int64_t ref_col_capacity, int32_t* row_ptr, int32_t* col_idx,
+                                       int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  wise_status st = check_build(bh, nq, 1, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity, workspace,
+                               workspace_bytes);
+  if (st != WISE_OK) return st;
+  int k;
+  switch (kind) {
+    case WISE_SUPPORT_STATIC:
+      if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
+      k = 0;
+      break;
+    case WISE_SUPPORT_SIZE_MATCHED:
+      k = 1;
+      break;
+    case WISE_SUPPORT_MASS_MATCHED:
+      k = 2;
+      break;
+    default:
+      return WISE_ERR_INVALID_ARG;
   }
-  hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, row_ptr, col_idx, nnz, plan, workspace,
-                                static_cast<hipStream_t>(stream));
+  if (k != 0) {
+    if (!ref_row_ptr || !ref_col_idx || ref_col_capacity < 0) return WISE_ERR_INVALID_ARG;
+    if (!aligned4(ref_row_ptr) || !aligned4(ref_col_idx)) return WISE_ERR_INVALID_ARG;
+  }
+  hipError_t e = launch_support(mass, bh, nq, 1, (double)eta, k, ref_row_ptr, ref_col_idx, ref_col_capacity, row_ptr,
+                                col_idx, nnz, plan, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
+}
+
+wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t* row_ptr, const int32_t* col_idx,
+                               int64_t col_capacity, float* retained, void* stream) {
+  if (bh <= 0 || nq <= 0 || nq > 4096 || (int64_t)bh * nq > INT32_MAX) return WISE_ERR_INVALID_ARG;
+  if (!mass || !row_ptr || !col_idx || !retained || col_capacity < 0) return WISE_ERR_INVALID_ARG;
+  if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(retained)) return WISE_ERR_INVALID_ARG;
+  hipError_t e = launch_retained_mass(mass, bh, nq, row_ptr, col_idx, col_capacity, retained,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 

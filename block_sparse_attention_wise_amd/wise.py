@@ -43,6 +43,11 @@ def _load():
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
     lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.wise_build_support_variant.restype = i32
+    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
+                                               ctypes.c_size_t, vp]
+    lib.wise_retained_mass.restype = i32
+    lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_sparse_attn.restype = i32
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, f32,
                                      vp]
@@ -196,6 +201,56 @@ def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspa
                                 *_plan_args(schedule), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "wise_build_support")
     return schedule
+
+
+SUPPORT_STATIC, SUPPORT_SIZE_MATCHED, SUPPORT_MASS_MATCHED = 0, 1, 2
+_VARIANTS = {"static": SUPPORT_STATIC, "size_matched": SUPPORT_SIZE_MATCHED, "mass_matched": SUPPORT_MASS_MATCHED}
+
+
+def build_support_variant(kind, mass, *, eta: float = 0.95, reference: Schedule | None = None,
+                          schedule: Schedule | None = None, workspace=None, stream=None, with_plan: bool = True):
+    """Intervention-control schedule from one step's masses [b*h, nq, nq] (fp32):
+    kind "static" (cumulative-eta support), "size_matched" or "mass_matched" (against
+    the reference schedule)."""
+    code = _VARIANTS[kind] if isinstance(kind, str) else int(kind)
+    if mass.dim() == 4 and mass.shape[0] == 1:
+        mass = mass[0]
+    if mass.dim() != 3 or mass.shape[1] != mass.shape[2]:
+        raise ValueError("mass must be [batch*heads, nq, nq]")
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
+        raise ValueError("mass must be a contiguous float32 device tensor")
+    bh, nq, _ = mass.shape
+    if code != SUPPORT_STATIC and reference is None:
+        raise ValueError("matched variants need the reference schedule")
+    if schedule is None:
+        schedule = alloc_schedule(bh, nq, mass.device, with_plan=with_plan)
+    if workspace is None:
+        workspace = torch.empty(max(build_support_workspace_bytes(bh, nq, 1), 16), dtype=torch.uint8,
+                                device=mass.device)
+    ref_rp = _ptr(reference.row_ptr) if reference is not None else None
+    ref_ci = _ptr(reference.col_idx) if reference is not None else None
+    ref_cap = reference.col_idx.numel() if reference is not None else 0
+    st = lib.wise_build_support_variant(code, bh, nq, _ptr(mass), float(eta), ref_rp, ref_ci, ref_cap,
+                                        _ptr(schedule.row_ptr), _ptr(schedule.col_idx), schedule.col_idx.numel(),
+                                        _ptr(schedule.nnz), *_plan_args(schedule), _ptr(workspace),
+                                        workspace.numel(), _stream(stream))
+    _check(st, "wise_build_support_variant")
+    return schedule
+
+
+def retained_mass(mass, schedule: Schedule, *, out=None, stream=None):
+    """Per-row retained mass of a schedule under one step's masses [b*h, nq, nq] -> fp32 [b*h*nq]."""
+    if mass.dim() != 3 or mass.shape[1] != mass.shape[2]:
+        raise ValueError("mass must be [batch*heads, nq, nq]")
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
+        raise ValueError("mass must be a contiguous float32 device tensor")
+    bh, nq, _ = mass.shape
+    out = _f32_buf(out, bh * nq, mass.device, "retained") if out is not None else torch.empty(
+        bh * nq, dtype=torch.float32, device=mass.device)
+    st = lib.wise_retained_mass(bh, nq, _ptr(mass), _ptr(schedule.row_ptr), _ptr(schedule.col_idx),
+                                schedule.col_idx.numel(), _ptr(out), _stream(stream))
+    _check(st, "wise_retained_mass")
+    return out
 
 
 def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=False, scale=None,

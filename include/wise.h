@@ -49,7 +49,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 2
+#define WISE_ABI_VERSION 3
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -134,6 +134,55 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                int32_t* nnz, int32_t* plan, int64_t plan_capacity,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Intervention-control schedules of the WISE paper (App. B, intervention
+ * controls), built from ONE step's block masses (normally step 1):
+ *   WISE_SUPPORT_STATIC        the cumulative-eta support of that step alone
+ *                              (Static-95 at eta = 0.95);
+ *   WISE_SUPPORT_SIZE_MATCHED  per row, the K_q blocks of largest mass (mass
+ *                              descending, lower block index first), K_q the
+ *                              number of distinct admissible blocks of the
+ *                              reference row (SizeMatched: TopK(a_q, K_q));
+ *   WISE_SUPPORT_MASS_MATCHED  per row, the smallest sorted prefix whose fp64
+ *                              cumulative mass reaches m_q - 1e-9, m_q the mass
+ *                              of this step that the reference row keeps (the
+ *                              paper's m_q^WISE), summed in the same sorted
+ *                              order; at least one block.
+ *   mass          : fp32 [bh][nq][nq], as written by wise_full_attn_mass.
+ *   eta           : WISE_SUPPORT_STATIC only, 0 < eta <= 1.
+ *   ref_row_ptr, ref_col_idx, ref_col_capacity : the reference schedule (the
+ *                   WISE working set), matched kinds only (may be NULL for
+ *                   STATIC); entries outside 0..q are ignored, duplicates count
+ *                   once.
+ *   the outputs, plan and workspace are as for wise_build_support (num_steps 1).
+ */
+typedef enum {
+  WISE_SUPPORT_STATIC = 0,
+  WISE_SUPPORT_SIZE_MATCHED = 1,
+  WISE_SUPPORT_MASS_MATCHED = 2
+} wise_support_variant;
+
+wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq, const float* mass, float eta,
+                                       const int32_t* ref_row_ptr, const int32_t* ref_col_idx,
+                                       int64_t ref_col_capacity, int32_t* row_ptr, int32_t* col_idx,
+                                       int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Retained attention mass of a schedule (the WISE paper, App. B: the fraction of
+ * full-attention mass a support keeps, "Future" in Tables 1, 5, 6 when the masses
+ * come from a late step):
+ *   retained[r] = sum of mass[r][b] over the distinct blocks b of schedule row r
+ *                 with 0 <= b <= q, accumulated in fp64, written as fp32.
+ *   mass : fp32 [bh][nq][nq] (wise_full_attn_mass of the step of interest).
+ *   row_ptr, col_idx, col_capacity : the schedule; offsets are clamped to
+ *                 0..col_capacity.
+ *   retained : fp32 [bh*nq], written.
+ */
+wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t* row_ptr,
+                               const int32_t* col_idx, int64_t col_capacity, float* retained,
+                               void* stream);
 
 /*
  * Late-step block-sparse causal attention over a CSR schedule.

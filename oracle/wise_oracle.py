@@ -148,6 +148,50 @@ def select_support(masses, eta):
     return np.sort(order[:kstar])
 
 
+def size_matched_support(masses, k):
+    """SizeMatched control of the WISE paper (App. B, intervention controls):
+    TopK(a_q, K_q), the K_q blocks of largest mass, equal masses to the lower
+    block index (the same order as the cumulative support).
+
+    masses: the q+1 admissible block masses of one step (step 1 in the paper);
+    k: K_q, the size of the WISE working set of the same query block.
+    Returns the selected block indices, ascending.
+    """
+    order = sorted_order(masses)
+    return np.sort(order[:max(0, min(int(k), order.shape[0]))])
+
+
+MASS_MATCH_SLACK = 1e-9
+
+
+def mass_matched_support(masses, reference, slack=MASS_MATCH_SLACK):
+    """MassMatched control of the WISE paper (App. B, intervention controls).
+
+    The paper defines the mass the WISE working set W_q keeps at step 1,
+    m_q = sum over j in W_q of a_{q,j}; the control is read here as the
+    cumulative support of the same step at threshold m_q: the smallest prefix
+    of the blocks sorted by mass whose running sum reaches m_q (at least one
+    block).  m_q is summed over W_q's blocks taken in that sorted order, and the
+    prefixes are compared with m_q - slack, so that a working set which is
+    itself a sorted prefix is matched exactly whatever the rounding of the two
+    fp64 sums.
+
+    masses: the q+1 admissible block masses of one step; reference: W_q.
+    Returns the selected block indices, ascending.
+    """
+    masses = _f64(masses)
+    order = sorted_order(masses)
+    ref = set(int(b) for b in np.asarray(reference).tolist() if 0 <= int(b) < masses.shape[0])
+    m = 0.0
+    for b in order:
+        if int(b) in ref:
+            m += masses[b]
+    c = np.cumsum(masses[order])
+    reached = np.nonzero(c >= m - slack)[0]
+    kstar = order.shape[0] if reached.size == 0 else int(reached[0]) + 1
+    return np.sort(order[:max(1, kstar)])
+
+
 def step_supports(r, eta):
     """Per-query-block supports of one head at one step: list of index arrays."""
     nq = r.shape[0]

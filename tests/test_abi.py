@@ -38,6 +38,9 @@ def lib():
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
     lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
+                                               ctypes.c_size_t, vp]
+    lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, f32,
                                      vp]
     lib.wise_status_string.restype = ctypes.c_char_p
@@ -49,14 +52,14 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"wise_full_attn_mass", "wise_dense_attn", "wise_build_support",
                           "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity",
-                          "wise_sparse_attn",
+                          "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
                           "wise_status_string", "wise_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in wise.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 2
+    assert lib.wise_abi_version() == 3
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -149,3 +152,29 @@ def test_sparse_validation(lib):
     assert sp(q=MIS) == INVALID
     assert sp(plan=P, pcap=1) == INVALID                # fewer than G + 1 = 2 entries
     assert sp(plan=ctypes.c_void_p(0x10002), pcap=64) == INVALID
+
+
+def test_variant_and_retained_validation(lib):
+    bh, nq = 2, 8
+    cap = bh * nq * (nq + 1) // 2
+    wsb = lib.wise_build_support_workspace_bytes(bh, nq, 1)
+
+    def var(kind=1, mass=P, eta=0.95, rrp=P, rci=P, rcap=10, rp=P, ci=P, c=cap, nnz=P, ws=P2, w=wsb):
+        return lib.wise_build_support_variant(kind, bh, nq, mass, eta, rrp, rci, rcap, rp, ci, c, nnz, NULL, 0,
+                                              ws, w, None)
+    assert var(kind=3) == INVALID and var(kind=-1) == INVALID
+    assert var(kind=0, eta=0.0) == INVALID and var(kind=0, eta=1.5) == INVALID
+    for kind in (1, 2):
+        assert var(kind=kind, rrp=NULL) == INVALID
+        assert var(kind=kind, rci=NULL) == INVALID
+        assert var(kind=kind, rcap=-1) == INVALID
+        assert var(kind=kind, rrp=ctypes.c_void_p(0x10002)) == INVALID
+    assert var(mass=NULL) == INVALID and var(c=cap - 1) == INVALID and var(w=8) == INVALID
+    assert var(ws=ctypes.c_void_p(0x10004)) == INVALID
+
+    def ret(bh_=bh, nq_=nq, mass=P, rp=P, ci=P, cap_=10, out=P2):
+        return lib.wise_retained_mass(bh_, nq_, mass, rp, ci, cap_, out, None)
+    assert ret(bh_=0) == INVALID and ret(nq_=0) == INVALID and ret(nq_=4097) == INVALID
+    for kw in (dict(mass=NULL), dict(rp=NULL), dict(ci=NULL), dict(out=NULL), dict(cap_=-1),
+               dict(out=ctypes.c_void_p(0x20002))):
+        assert ret(**kw) == INVALID, kw
