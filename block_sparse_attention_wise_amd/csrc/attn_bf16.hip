@@ -34,7 +34,7 @@ struct Tile {
   static constexpr int NC = D / 16;        // 16-wide k chunks of Q K^T
   static constexpr int HALF = D / 2;       // elements of a row owned by one lane half
   static constexpr int NT = D / 32;        // 32-wide column tiles of O
-  static constexpr int VSTRIDE = D + 32;   // V tile row stride (elements); 2*VSTRIDE = 64 mod
+  static constexpr int VSTRIDE = D == 96 ? D : D + 32;  // V tile row stride (elements); 2*VSTRIDE = 64 or 192 mod
                                            // 256 bytes keeps the transposing reads conflict free
   static constexpr int KSTRIDE = D + 8;    // K tile row stride (elements); 16-byte reads of 16
                                            // consecutive rows hit distinct banks
@@ -323,7 +323,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   constexpr int NTHR = 64 * W;
   constexpr int CHUNKS = 32 * T::C8;                // 16-byte chunks of one tile
   constexpr int CPT = (CHUNKS + NTHR - 1) / NTHR;  // ... per thread
-  static_assert(CPT * NTHR == CHUNKS || CPT == 1, "tile chunks per thread");
+  static_assert(CPT * NTHR >= CHUNKS, "tile chunks per thread");
   // tiles per trip: the sparse lists are short and scattered, so their trips are
   // longer (fewer barriers, more loads in flight)
   constexpr int TRIP = SPARSE ? kSparseTrip : 2;
@@ -337,17 +337,24 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   const int ngroups = (a.nq + W - 1) / W;
   const int bhn = a.rows / a.nq;
   // Longest-first order over all heads: workgroup p takes the (p / bhn)-th longest
-  // query group of head p % bhn.  Consecutive workgroups land on different XCDs,
-  // so each XCD sees the heads congruent to it modulo 8 (bhn a multiple of 8).
-  const int bh = blockIdx.x % bhn;
+  // query group of head slot s = p % bhn.  Consecutive workgroups land on
+  // different XCDs (XCD s mod 8 when bhn is a multiple of 8); slot s maps to head
+  // (s mod 8) * bhn/8 + s / 8, so each XCD works on one contiguous run of heads,
+  // and the query heads of one key-value group share that XCD's L2.
+  const int slot = blockIdx.x % bhn;
+  const int bh = (bhn & 7) == 0 ? (slot & 7) * (bhn >> 3) + (slot >> 3) : slot;
   const int grp = ngroups - 1 - (int)(blockIdx.x / bhn);
   const int q0 = W * grp;
   const int qb = q0 + wave;
   const bool active = qb < a.nq;
   const int qlast = min(q0 + W, a.nq) - 1;
   const size_t head_off = (size_t)bh * a.seqlen * D;
-  const __bf16* kh = a.k + head_off;
-  const __bf16* vh = a.v + head_off;
+  // grouped-query attention: query head h of batch b reads key-value head
+  // b * (heads / kv_group) + h / kv_group
+  const int bb = bh / a.heads, hq = bh - bb * a.heads;
+  const size_t kv_off = (size_t)(bb * (a.heads / a.kv_group) + hq / a.kv_group) * a.seqlen * D;
+  const __bf16* kh = a.k + kv_off;
+  const __bf16* vh = a.v + kv_off;
 
   // Q^T operand; inactive wavefronts (past the last query block) read a valid row
   // and discard it, so the load is unconditional and completes before the loop
@@ -542,7 +549,14 @@ hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bo
   const int bhn = a.rows / a.nq;
   const int w = sparse ? kSparseWaves : kWaves;
   const dim3 grid(bhn * ((a.nq + w - 1) / w)), block(64 * w);
-  if (head_dim == 128) {
+  if (head_dim == 96) {
+    if (sparse)
+      hipLaunchKernelGGL((attn_sparse_kernel<96>), grid, block, 0, stream, a);
+    else if (mass)
+      hipLaunchKernelGGL((attn_dense_kernel<96, kDenseMass>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_dense_kernel<96, kDense>), grid, block, 0, stream, a);
+  } else if (head_dim == 128) {
     if (sparse)
       hipLaunchKernelGGL((attn_sparse_kernel<128>), grid, block, 0, stream, a);
     else if (mass)

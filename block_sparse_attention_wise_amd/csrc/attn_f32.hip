@@ -42,6 +42,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   const int qb = a.nq - 1 - (logical - bh * a.nq);
   const int row = bh * a.nq + qb;
   const size_t head_off = (size_t)bh * a.seqlen * D;
+  const int bb = bh / a.heads, hq = bh - bb * a.heads;
+  const size_t kv_off = (size_t)(bb * (a.heads / a.kv_group) + hq / a.kv_group) * a.seqlen * D;
   const float* qh = a.q + head_off + (size_t)(32 * qb) * D;
 
   for (int e = tid; e < 32 * D; e += 256) qs[(e / D) * S + e % D] = qh[e];
@@ -65,8 +67,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
     const int b = SPARSE ? a.col_idx[it] : it;
     if (SPARSE && (b < 0 || b > qb)) continue;
     __syncthreads();
-    const float* kb = a.k + head_off + (size_t)(32 * b) * D;
-    const float* vb = a.v + head_off + (size_t)(32 * b) * D;
+    const float* kb = a.k + kv_off + (size_t)(32 * b) * D;
+    const float* vb = a.v + kv_off + (size_t)(32 * b) * D;
     for (int e = tid; e < 32 * D; e += 256) {
       ks[(e / D) * S + e % D] = kb[e];
       vs[(e / D) * S + e % D] = vb[e];
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
     float* mrow = a.mass + (size_t)row * a.nq;
     for (int b = 0; b <= qb; ++b) {
       __syncthreads();
-      const float* kb = a.k + head_off + (size_t)(32 * b) * D;
+      const float* kb = a.k + kv_off + (size_t)(32 * b) * D;
       for (int e = tid; e < 32 * D; e += 256) ks[(e / D) * S + e % D] = kb[e];
       __syncthreads();
       float part = 0.f;
@@ -148,6 +150,10 @@ hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool
   if (head_dim == 128) {
     if (sparse) return launch<128, true, false>(a, stream);
     return mass ? launch<128, false, true>(a, stream) : launch<128, false, false>(a, stream);
+  }
+  if (head_dim == 96) {
+    if (sparse) return launch<96, true, false>(a, stream);
+    return mass ? launch<96, false, true>(a, stream) : launch<96, false, false>(a, stream);
   }
   if (sparse) return launch<64, true, false>(a, stream);
   return mass ? launch<64, false, true>(a, stream) : launch<64, false, false>(a, stream);

@@ -27,6 +27,8 @@ struct AttnBf16Args {
   int seqlen;
   int nq;
   int rows;                  // batch * heads * nq
+  int heads;                 // query heads per batch entry
+  int kv_group;              // query heads per key-value head (grouped-query attention)
   float scale_log2;          // softmax scale * log2(e)
 };
 
@@ -43,6 +45,8 @@ struct AttnF32Args {
   int seqlen;
   int nq;
   int rows;
+  int heads;
+  int kv_group;
   float scale;               // softmax scale (natural-log units)
 };
 

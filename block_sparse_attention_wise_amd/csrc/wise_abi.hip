@@ -16,18 +16,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Shape checks shared by the attention entry points.  Returns WISE_OK or the error.
-wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
-                             const void* q, const void* k, const void* v, const void* o, const float* lse,
-                             float scale) {
+wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim,
+                             int block, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, float scale) {
   if (dt != WISE_BF16 && dt != WISE_FP32) return WISE_ERR_INVALID_ARG;
   if (batch <= 0 || heads <= 0 || seqlen <= 0 || head_dim <= 0 || block <= 0) return WISE_ERR_INVALID_ARG;
+  if (kv_heads <= 0 || kv_heads > heads || heads % kv_heads != 0) return WISE_ERR_INVALID_ARG;
   if (!q || !k || !v || !o) return WISE_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WISE_ERR_INVALID_ARG;
   if (lse && !aligned4(lse)) return WISE_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return WISE_ERR_INVALID_ARG;
   if (block != kBlock) return WISE_ERR_UNSUPPORTED;
   if (seqlen % block != 0) return WISE_ERR_INVALID_ARG;
-  if (head_dim != 64 && head_dim != 128) return WISE_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 96 && head_dim != 128) return WISE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)batch * heads * (seqlen / block);
   const int64_t elems = (int64_t)batch * heads * seqlen * head_dim;
   if (rows > INT32_MAX || elems > ((int64_t)1 << 40)) return WISE_ERR_INVALID_ARG;
@@ -36,8 +37,8 @@ wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int seqlen, in
 
 float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim); }
 
-wise_status run_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, const void* q, const void* k,
-                     const void* v, void* o, float* lse, float* mass, const int32_t* row_ptr,
+wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, const void* q,
+                     const void* k, const void* v, void* o, float* lse, float* mass, const int32_t* row_ptr,
                      const int32_t* col_idx, int64_t col_cap, const int32_t* plan, int64_t plan_cap, bool sparse,
                      float scale, void* stream) {
   if (col_cap > INT32_MAX) col_cap = INT32_MAX;
@@ -49,11 +50,12 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_d
   if (dt == WISE_BF16) {
     AttnBf16Args a{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
                    static_cast<__bf16*>(o), lse, mass, row_ptr, col_idx, col_cap, plan, plan_cap, seqlen, nq, rows,
-                   sc * 1.4426950408889634f};
+                   heads, heads / kv_heads, sc * 1.4426950408889634f};
     e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
   } else {
     AttnF32Args a{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-                  static_cast<float*>(o), lse, mass, row_ptr, col_idx, col_cap, seqlen, nq, rows, sc};
+                  static_cast<float*>(o), lse, mass, row_ptr, col_idx, col_cap, seqlen, nq, rows, heads,
+                  heads / kv_heads, sc};
     e = launch_attn_f32(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
@@ -97,20 +99,21 @@ const char* wise_status_string(wise_status s) {
   return "unknown status";
 }
 
-wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
-                                const void* q, const void* k, const void* v, void* o, float* lse, float* mass,
-                                float scale, void* stream) {
-  wise_status st = check_attn_shape(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
+wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim,
+                                int block, const void* q, const void* k, const void* v, void* o, float* lse,
+                                float* mass, float scale, void* stream) {
+  wise_status st = check_attn_shape(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
   if (st != WISE_OK) return st;
   if (mass && !aligned4(mass)) return WISE_ERR_INVALID_ARG;
-  return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, mass, nullptr, nullptr, 0, nullptr, 0, false,
-                  scale, stream);
+  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, q, k, v, o, lse, mass, nullptr, nullptr, 0, nullptr,
+                  0, false, scale, stream);
 }
 
-wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
+wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
                             const void* q, const void* k, const void* v, void* o, float* lse, float scale,
                             void* stream) {
-  return wise_full_attn_mass(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, scale, stream);
+  return wise_full_attn_mass(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, scale,
+                             stream);
 }
 
 size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps) {
@@ -179,11 +182,11 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
-wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim, int block,
+wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
                              const void* q, const void* k, const void* v, void* o, float* lse,
                              const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
                              const int32_t* plan, int64_t plan_capacity, float scale, void* stream) {
-  wise_status st = check_attn_shape(dt, batch, heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
+  wise_status st = check_attn_shape(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
   if (st != WISE_OK) return st;
   if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
   if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
@@ -193,7 +196,8 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, in
     if (!aligned4(plan) || plan_capacity < groups + 1) return WISE_ERR_INVALID_ARG;
     if (dt != WISE_BF16) plan = nullptr;  // the fp32 kernel walks the CSR rows
   }
-  return run_attn(dt, batch, heads, seqlen, head_dim, q, k, v, o, lse, nullptr, row_ptr, col_idx, col_capacity,
+  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, q, k, v, o, lse, nullptr, row_ptr, col_idx,
+                  col_capacity,
                   plan, plan_capacity, true, scale, stream);
 }
 

@@ -26,6 +26,12 @@ not available; these synthetic inputs stand in for them.  Recipe, per head h:
 Random streams: numpy PCG64 seeded with [cfg_seed, head, step, stream] where
 stream is 0/1/2 for Q/K/V, 3 for the relevance draw, 4 for the sink direction;
 the base tensors use step 0.
+
+Grouped-query workloads (kv_heads < heads, the Recurrent-Llama geometry of the
+WISE paper, App. B) draw K, V and the sink direction per key-value head g (head
+index g in the seeds) and Q and the relevance draw per query head h; query head
+h reads key-value head h // (heads / kv_heads), and its planted relevance is the
+mean of that head's keys.  With kv_heads = heads this is the recipe above.
 """
 from __future__ import annotations
 
@@ -51,10 +57,19 @@ class Workload:
     etas: tuple         # eta values the workload is run at (first is the default)
     seed: int
     batch: int = 1
+    kv_heads: int = 0   # 0: one key-value head per query head
 
     @property
     def nq(self) -> int:
         return self.seqlen // BLOCK
+
+    @property
+    def kvh(self) -> int:
+        return self.kv_heads or self.heads
+
+    @property
+    def group(self) -> int:
+        return self.heads // self.kvh
 
 
 WORKLOADS = {
@@ -63,6 +78,13 @@ WORKLOADS = {
     "2k": Workload("2k", "bf16", 32, 128, 2048, 4, True, (0.95,), 2),
     "4k": Workload("4k", "bf16", 32, 128, 4096, 4, True, (0.95,), 3),
     "16k": Workload("16k", "bf16", 32, 128, 16384, 6, True, (0.90, 0.95, 0.99), 4),
+    # the pages' geometries (App. B): Huginn, d = 96 with 55 heads per recurrent
+    # layer; Recurrent-Llama, grouped-query attention with 32 query / 8 key-value
+    # heads of d = 64; plus small cases of each for full parity
+    "d96": Workload("d96", "bf16", 5, 96, 1024, 3, True, (0.95,), 5),
+    "gqa": Workload("gqa", "bf16", 8, 64, 1024, 3, True, (0.95,), 6, kv_heads=2),
+    "huginn4k": Workload("huginn4k", "bf16", 55, 96, 4096, 4, True, (0.95,), 7),
+    "llama4k": Workload("llama4k", "bf16", 32, 64, 4096, 4, True, (0.95,), 8, kv_heads=8),
 }
 
 
@@ -70,12 +92,24 @@ def _rng(seed, head, step, stream):
     return np.random.default_rng([int(seed), int(head), int(step), int(stream)])
 
 
-def base_head(w: Workload, head: int, planted: str = "scaled"):
-    """Base (step-independent) Q, K, V of one head as float32 [n, d] arrays."""
+def base_kv(w: Workload, g: int):
+    """Base K, V of key-value head g as float32 [n, d] arrays, before the sink."""
+    n, d = w.seqlen, w.head_dim
+    k = _rng(w.seed, g, 0, 1).standard_normal((n, d), dtype=np.float32)
+    v = _rng(w.seed, g, 0, 2).standard_normal((n, d), dtype=np.float32)
+    return k, v
+
+
+def sink_vector(w: Workload, g: int):
+    d = w.head_dim
+    u = _rng(w.seed, g, 0, 4).standard_normal(d)
+    return (u / np.linalg.norm(u) * np.sqrt(2.0 * np.sqrt(d))).astype(np.float32)
+
+
+def base_q(w: Workload, head: int, k, planted: str = "scaled"):
+    """Base Q of query head ``head`` given its key-value head's base keys k."""
     n, d = w.seqlen, w.head_dim
     q = _rng(w.seed, head, 0, 0).standard_normal((n, d), dtype=np.float32)
-    k = _rng(w.seed, head, 0, 1).standard_normal((n, d), dtype=np.float32)
-    v = _rng(w.seed, head, 0, 2).standard_normal((n, d), dtype=np.float32)
     rel = _rng(w.seed, head, 0, 3)
     nq = n // BLOCK
     for qb in range(1, nq):
@@ -91,23 +125,34 @@ def base_head(w: Workload, head: int, planted: str = "scaled"):
             raise ValueError(f"unknown planted mode {planted!r}")
         q[qb * BLOCK:(qb + 1) * BLOCK] += add.astype(np.float32)
     if w.sink:
-        u = _rng(w.seed, head, 0, 4).standard_normal(d)
-        u = (u / np.linalg.norm(u) * np.sqrt(2.0 * np.sqrt(d))).astype(np.float32)
-        q += u
-        k[:BLOCK] += u
+        q += sink_vector(w, head // w.group)
+    return q
+
+
+def base_head(w: Workload, head: int, planted: str = "scaled"):
+    """Base (step-independent) Q, K, V of one query head (K, V of its key-value
+    head) as float32 [n, d] arrays."""
+    g = head // w.group
+    k, v = base_kv(w, g)
+    q = base_q(w, head, k, planted)
+    if w.sink:
+        k[:BLOCK] += sink_vector(w, g)
     return q, k, v
 
 
-def drift_head(w: Workload, head: int, step: int, base):
-    """Q, K, V of one head at recurrent step ``step`` (1-based), float32."""
+def drift(w: Workload, head: int, step: int, stream: int, x):
+    """x at recurrent step ``step`` (1-based): x + (0.05 / step) N(0, 1)."""
     if not 1 <= step <= T_STEPS:
         raise ValueError("recurrent steps are numbered 1..32")
-    amp = np.float32(0.05 / step)
-    out = []
-    for stream, x in enumerate(base):
-        noise = _rng(w.seed, head, step, stream).standard_normal(x.shape, dtype=np.float32)
-        out.append(x + amp * noise)
-    return tuple(out)
+    noise = _rng(w.seed, head, step, stream).standard_normal(x.shape, dtype=np.float32)
+    return x + np.float32(0.05 / step) * noise
+
+
+def drift_head(w: Workload, head: int, step: int, base):
+    """Q, K, V of one head at recurrent step ``step`` (1-based), float32 (K, V
+    drawn with the key-value head's seeds)."""
+    g = head // w.group
+    return (drift(w, head, step, 0, base[0]), drift(w, g, step, 1, base[1]), drift(w, g, step, 2, base[2]))
 
 
 def _threads():
@@ -117,21 +162,38 @@ def _threads():
 class Generator:
     """Caches the base tensors of a workload and produces per-step inputs.
 
-    heads: optional subset of head indices (default all).
+    heads: optional subset of query-head indices (default all).  Q has one slice
+    per listed head; K and V have one slice per key-value head those heads read,
+    in order of first use (all key-value heads when ``heads`` is None), so with
+    one key-value head per query head the three tensors line up head by head.
     """
 
     def __init__(self, w: Workload, heads=None, planted: str = "scaled"):
         self.w = w
         self.heads = list(range(w.heads)) if heads is None else list(heads)
+        self.kv = []
+        for h in self.heads:
+            if h // w.group not in self.kv:
+                self.kv.append(h // w.group)
         with _cf.ThreadPoolExecutor(_threads()) as ex:
-            self.base = list(ex.map(lambda h: base_head(w, h, planted), self.heads))
+            kv = dict(zip(self.kv, ex.map(lambda g: base_kv(w, g), self.kv)))
+            self.base_q = list(ex.map(lambda h: base_q(w, h, kv[h // w.group][0], planted), self.heads))
+        self.base_kv = []
+        for g in self.kv:
+            k, v = kv[g]
+            if w.sink:
+                k = k.copy()
+                k[:BLOCK] += sink_vector(w, g)
+            self.base_kv.append((k, v))
 
     def step_f32(self, step: int):
-        """float32 arrays [len(heads), n, d] for Q, K, V at ``step``."""
+        """float32 arrays Q [len(heads), n, d], K and V [len(kv heads), n, d] at ``step``."""
+        w = self.w
         with _cf.ThreadPoolExecutor(_threads()) as ex:
-            per_head = list(ex.map(lambda i: drift_head(self.w, self.heads[i], step, self.base[i]),
-                                   range(len(self.heads))))
-        return tuple(np.stack([ph[j] for ph in per_head]) for j in range(3))
+            q = list(ex.map(lambda i: drift(w, self.heads[i], step, 0, self.base_q[i]), range(len(self.heads))))
+            kv = list(ex.map(lambda j: (drift(w, self.kv[j], step, 1, self.base_kv[j][0]),
+                                        drift(w, self.kv[j], step, 2, self.base_kv[j][1])), range(len(self.kv))))
+        return np.stack(q), np.stack([x[0] for x in kv]), np.stack([x[1] for x in kv])
 
     def step_torch(self, step: int, device="cpu"):
         """Q, K, V at ``step`` as torch tensors [batch=1, heads, n, d] in the

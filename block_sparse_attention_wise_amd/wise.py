@@ -19,9 +19,11 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
+ABI_VERSION = 4
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_dense_attn",
-    "wise_build_support_workspace_bytes", "wise_build_support", "wise_sparse_attn",
+    "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity", "wise_build_support",
+    "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
 )
 
 
@@ -31,12 +33,14 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.wise_abi_version.restype = i32
+    if lib.wise_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.wise_abi_version()}, this binding needs {ABI_VERSION}")
     lib.wise_status_string.restype = ctypes.c_char_p
     lib.wise_status_string.argtypes = [i32]
     lib.wise_full_attn_mass.restype = i32
-    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
     lib.wise_dense_attn.restype = i32
-    lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
     lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
     lib.wise_build_support.restype = i32
@@ -49,8 +53,8 @@ def _load():
     lib.wise_retained_mass.restype = i32
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_sparse_attn.restype = i32
-    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, f32,
-                                     vp]
+    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
+                                     f32, vp]
     return lib
 
 
@@ -87,14 +91,22 @@ def _dtype_code(t):
 
 
 def _qkv_shape(q, k, v):
-    if q.dim() != 4:
+    """(batch, heads, kv_heads, seqlen, head_dim); k and v may have fewer heads
+    (grouped-query attention: a divisor of q's heads)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [batch, heads, seqlen, head_dim]")
+    b, h, n, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k and v must be [batch, kv_heads, seqlen, head_dim] matching q")
+    hk = k.shape[1]
+    if hk <= 0 or h % hk != 0:
+        raise ValueError("kv heads must divide the query heads")
     for t in (q, k, v):
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v must share shape, dtype and device")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share dtype and device")
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
-    return q.shape
+    return b, h, hk, n, d
 
 
 def _out_like(q, out):
@@ -119,7 +131,7 @@ def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, wa
 
     Returns (out, lse, mass); lse / mass are None unless passed or requested.
     """
-    b, h, n, d = _qkv_shape(q, k, v)
+    b, h, hk, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     nq = n // block
     if want_lse and lse is None:
@@ -128,7 +140,7 @@ def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, wa
         mass = torch.empty((b * h, nq, nq), dtype=torch.float32, device=q.device)
     lse = _f32_buf(lse, b * h * n, q.device, "lse")
     mass = _f32_buf(mass, b * h * nq * nq, q.device, "mass")
-    st = lib.wise_full_attn_mass(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+    st = lib.wise_full_attn_mass(_dtype_code(q), b, h, hk, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                  _ptr(lse), _ptr(mass), float(scale or 0.0), _stream(stream))
     _check(st, "wise_full_attn_mass")
     return out, lse, mass
@@ -136,12 +148,12 @@ def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, wa
 
 def dense_attn(q, k, v, *, out=None, lse=None, want_lse=False, scale=None, block=BLOCK, stream=None):
     """Dense causal attention (the in-run baseline).  Returns (out, lse)."""
-    b, h, n, d = _qkv_shape(q, k, v)
+    b, h, hk, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     if want_lse and lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
     lse = _f32_buf(lse, b * h * n, q.device, "lse")
-    st = lib.wise_dense_attn(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+    st = lib.wise_dense_attn(_dtype_code(q), b, h, hk, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                              _ptr(lse), float(scale or 0.0), _stream(stream))
     _check(st, "wise_dense_attn")
     return out, lse
@@ -257,7 +269,7 @@ def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=Fal
                 block=BLOCK, stream=None):
     """Block-sparse causal attention over a CSR schedule (walking its execution plan when it
     carries one).  Returns (out, lse)."""
-    b, h, n, d = _qkv_shape(q, k, v)
+    b, h, hk, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     if want_lse and lse is None:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
@@ -267,7 +279,7 @@ def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=Fal
             raise ValueError("schedule tensors must be contiguous int32 on q's device")
     if schedule.row_ptr.numel() < b * h * (n // block) + 1:
         raise ValueError("row_ptr too short for this shape")
-    st = lib.wise_sparse_attn(_dtype_code(q), b, h, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+    st = lib.wise_sparse_attn(_dtype_code(q), b, h, hk, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                               _ptr(lse), _ptr(schedule.row_ptr), _ptr(schedule.col_idx),
                               schedule.col_idx.numel(), *_plan_args(schedule), float(scale or 0.0),
                               _stream(stream))

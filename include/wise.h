@@ -12,9 +12,13 @@
  * fresh Q/K/V of steps 13..32.
  *
  * Conventions shared by every entry point
- *   - Tensors are batch-major, head-major, row-major: q, k, v, o are
- *     [batch][heads][seqlen][head_dim] contiguous; "row" r = (b*heads + h)*nq + qb
- *     indexes a (batch, head, query block) triple, nq = seqlen / block.
+ *   - Tensors are batch-major, head-major, row-major: q, o are
+ *     [batch][heads][seqlen][head_dim] contiguous, k, v are
+ *     [batch][kv_heads][seqlen][head_dim] (grouped-query attention when
+ *     kv_heads < heads: query head h reads key-value head h / (heads / kv_heads);
+ *     kv_heads must divide heads; kv_heads = heads is plain multi-head attention);
+ *     "row" r = (b*heads + h)*nq + qb indexes a (batch, query head, query block)
+ *     triple, nq = seqlen / block.
  *   - Every pointer argument is a DEVICE pointer owned by the caller, 16-byte
  *     aligned.  The library allocates nothing and keeps no state between calls,
  *     so concurrent calls on different streams are safe.
@@ -24,8 +28,8 @@
  *     argument nothing is launched and WISE_ERR_INVALID_ARG (or
  *     WISE_ERR_UNSUPPORTED for a valid but unimplemented shape) is returned.
  *     WISE_ERR_HIP reports a failed launch.
- *   - Only block = 32 and head_dim in {64, 128} are implemented; seqlen must be a
- *     positive multiple of block.  scale <= 0 selects 1/sqrt(head_dim).
+ *   - Only block = 32 and head_dim in {64, 96, 128} are implemented; seqlen must be
+ *     a positive multiple of block.  scale <= 0 selects 1/sqrt(head_dim).
  */
 #ifndef WISE_H_
 #define WISE_H_
@@ -49,7 +53,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 3
+#define WISE_ABI_VERSION 4
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -71,14 +75,14 @@ const char* wise_status_string(wise_status s);
  *                sweep over the keys once each row's log-sum-exp is known.
  * With mass == NULL this is the dense baseline kernel.
  */
-wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
-                                int block, const void* q, const void* k, const void* v, void* o,
-                                float* lse, float* mass, float scale, void* stream);
+wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
+                                int head_dim, int block, const void* q, const void* k, const void* v,
+                                void* o, float* lse, float* mass, float scale, void* stream);
 
 /* Dense causal attention: wise_full_attn_mass with mass = NULL. */
-wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
-                            int block, const void* q, const void* k, const void* v, void* o,
-                            float* lse, float scale, void* stream);
+wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
+                            int head_dim, int block, const void* q, const void* k, const void* v,
+                            void* o, float* lse, float scale, void* stream);
 
 /*
  * Bytes of device workspace wise_build_support needs for bh = batch*heads rows of
@@ -208,8 +212,8 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  * produces one).  The bf16 kernel supports up to 4096 key blocks per head
  * (seqlen <= 131072); beyond that it returns WISE_ERR_UNSUPPORTED.
  */
-wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int seqlen, int head_dim,
-                             int block, const void* q, const void* k, const void* v, void* o,
+wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
+                             int head_dim, int block, const void* q, const void* k, const void* v, void* o,
                              float* lse, const int32_t* row_ptr, const int32_t* col_idx,
                              int64_t col_capacity, const int32_t* plan, int64_t plan_capacity,
                              float scale, void* stream);

@@ -31,8 +31,8 @@ def lib():
         pytest.fail("libwise.so is not built (run python -m block_sparse_attention_wise_amd.build)")
     lib = ctypes.CDLL(LIB)
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
-    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
-    lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
     lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
@@ -41,8 +41,8 @@ def lib():
     lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
                                                ctypes.c_size_t, vp]
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
-    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, f32,
-                                     vp]
+    lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
+                                     f32, vp]
     lib.wise_status_string.restype = ctypes.c_char_p
     lib.wise_status_string.argtypes = [i32]
     return lib
@@ -59,14 +59,15 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 3
+    assert lib.wise_abi_version() == 4
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
 
 
-def _attn(lib, dt=BF16, b=1, h=2, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, mass=None, scale=0.0):
-    return lib.wise_full_attn_mass(dt, b, h, n, d, blk, q, k, v, o, lse, mass, scale, None)
+def _attn(lib, dt=BF16, b=1, h=2, hk=None, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, mass=None,
+          scale=0.0):
+    return lib.wise_full_attn_mass(dt, b, h, h if hk is None else hk, n, d, blk, q, k, v, o, lse, mass, scale, None)
 
 
 def test_attention_validation(lib):
@@ -79,13 +80,15 @@ def test_attention_validation(lib):
     assert _attn(lib, n=100) == INVALID                 # seqlen not a multiple of the block
     assert _attn(lib, blk=64) == UNSUPPORTED
     assert _attn(lib, blk=16) == UNSUPPORTED
-    assert _attn(lib, d=96) == UNSUPPORTED
+    assert _attn(lib, d=80) == UNSUPPORTED
+    for hk in (0, -1, 3, 4):                         # kv heads must divide heads (h = 2) and not exceed it
+        assert _attn(lib, hk=hk) == INVALID, hk
     assert _attn(lib, lse=ctypes.c_void_p(0x10002)) == INVALID
     assert _attn(lib, mass=ctypes.c_void_p(0x10001)) == INVALID
     assert _attn(lib, scale=float("nan")) == INVALID
     assert _attn(lib, scale=float("inf")) == INVALID
-    assert lib.wise_dense_attn(BF16, 1, 1, 64, 128, 32, P, P, P, NULL, None, 0.0, None) == INVALID
-    assert lib.wise_dense_attn(FP32, 1, 1, 64, 96, 32, P, P, P, P2, None, 0.0, None) == UNSUPPORTED
+    assert lib.wise_dense_attn(BF16, 1, 1, 1, 64, 128, 32, P, P, P, NULL, None, 0.0, None) == INVALID
+    assert lib.wise_dense_attn(FP32, 1, 1, 1, 64, 80, 32, P, P, P, P2, None, 0.0, None) == UNSUPPORTED
 
 
 def test_workspace_bytes(lib):
@@ -136,10 +139,10 @@ def test_build_support_validation(lib):
 
 def test_sparse_validation(lib):
     def sp(**kw):
-        a = dict(dt=BF16, b=1, h=1, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, rp=P, ci=P, cap=10,
+        a = dict(dt=BF16, b=1, h=1, hk=1, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, rp=P, ci=P, cap=10,
                  plan=NULL, pcap=0, scale=0.0)
         a.update(kw)
-        return lib.wise_sparse_attn(a["dt"], a["b"], a["h"], a["n"], a["d"], a["blk"], a["q"], a["k"], a["v"],
+        return lib.wise_sparse_attn(a["dt"], a["b"], a["h"], a["hk"], a["n"], a["d"], a["blk"], a["q"], a["k"], a["v"],
                                     a["o"], a["lse"], a["rp"], a["ci"], a["cap"], a["plan"], a["pcap"], a["scale"],
                                     None)
     assert sp(rp=NULL) == INVALID
@@ -150,6 +153,8 @@ def test_sparse_validation(lib):
     assert sp(d=256) == UNSUPPORTED
     assert sp(n=32 * 4097) == UNSUPPORTED              # bf16 rows beyond 4096 key blocks
     assert sp(q=MIS) == INVALID
+    assert sp(hk=2) == INVALID                          # more kv heads than query heads
+    assert sp(d=80) == UNSUPPORTED
     assert sp(plan=P, pcap=1) == INVALID                # fewer than G + 1 = 2 entries
     assert sp(plan=ctypes.c_void_p(0x10002), pcap=64) == INVALID
 

@@ -16,7 +16,11 @@ DEV = "cuda"
 CASES = {
     "4k": dict(heads=[0, 11, 22, 31], qblocks=None),                       # every query block of 4 heads
     "16k": dict(heads=[0, 31], qblocks=[0, 1, 2, 77, 255, 256, 400, 510, 511]),
+    # the pages' geometries: Huginn (55 heads, d = 96), Recurrent-Llama (32 query / 8 kv heads, d = 64)
+    "huginn4k": dict(heads=[0, 27, 54], qblocks=[0, 1, 5, 63, 64, 100, 126, 127]),
+    "llama4k": dict(heads=[0, 3, 4, 31], qblocks=[0, 1, 5, 63, 64, 100, 126, 127]),
 }
+FULL = ["4k", "16k", "huginn4k", "llama4k"]
 
 
 def _run_gpu(name):
@@ -34,7 +38,7 @@ def _run_gpu(name):
     return wise, w, g, mass, host
 
 
-@pytest.mark.parametrize("name", ["4k", "16k"])
+@pytest.mark.parametrize("name", FULL)
 def test_fullsize_schedule_and_sparse_attention(name):
     wise, w, g, mass, host = _run_gpu(name)
     case = CASES[name]
@@ -45,7 +49,7 @@ def test_fullsize_schedule_and_sparse_attention(name):
     orc = {}
     for h in case["heads"]:
         for t in (9, 10, 11, 12):
-            qh, kh = f64(host[t][0][0, h]), f64(host[t][1][0, h])
+            qh, kh = f64(host[t][0][0, h]), f64(host[t][1][0, h // w.group])
             for qb in qbs:
                 r = O.block_mass(qh, kh, qblocks=(qb, qb + 1))[0]
                 orc[(h, t, qb)] = r
@@ -61,7 +65,7 @@ def test_fullsize_schedule_and_sparse_attention(name):
         assert int(sched.nnz.item()) == int(sched.row_ptr[-1].item())
         flagged_total = 0
         for h in case["heads"]:
-            qh, kh, vh = f64(q13[0, h]), f64(k13[0, h]), f64(v13[0, h])
+            qh, kh, vh = f64(q13[0, h]), f64(k13[0, h // w.group]), f64(v13[0, h // w.group])
             sup_rows = [np.array([0])] * w.nq
             for qb in qbs:
                 sup, flags = oracle_union_row([orc[(h, t, qb)][:qb + 1] for t in (9, 10, 11, 12)], eta)
@@ -79,7 +83,7 @@ def test_fullsize_schedule_and_sparse_attention(name):
         note(f"{name} eta={eta}: flagged mismatching blocks {flagged_total}")
 
 
-@pytest.mark.parametrize("name", ["4k", "16k"])
+@pytest.mark.parametrize("name", FULL)
 def test_fullsize_dense_rows(name):
     from block_sparse_attention_wise_amd import wise
     w = WORKLOADS[name]
@@ -91,7 +95,7 @@ def test_fullsize_dense_rows(name):
     torch.cuda.synchronize()
     qbs = case["qblocks"] if case["qblocks"] is not None else [0, 1, w.nq // 2, w.nq - 1]
     for h in case["heads"]:
-        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group])
         for qb in qbs:
             ro, rl = O.causal_attention(qh, kh, vh, rows=(32 * qb, 32 * qb + 32))
             sl = slice(32 * qb, 32 * qb + 32)

@@ -15,7 +15,7 @@ from parity_helpers import (assert_attn_close, assert_lse_close, assert_mass_clo
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-SMALL = ["tiny", "1k", "2k"]
+SMALL = ["tiny", "1k", "2k", "d96", "gqa"]   # d96: head_dim 96; gqa: 8 query / 2 key-value heads
 
 
 def _wise():
@@ -40,7 +40,7 @@ def test_dense_attention(name):
     o, lse = wise.dense_attn(*dev, want_lse=True)
     torch.cuda.synchronize()
     for h in range(w.heads):
-        ro, rl = O.causal_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]))
+        ro, rl = O.causal_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]))
         assert_attn_close(f64(o[0, h]), ro, w.dtype, f"{name} head {h} O")
         assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} head {h}")
 
@@ -53,7 +53,7 @@ def test_discovery_attention_and_block_mass(name):
     o, lse, mass = wise.full_attn_mass(*dev, want_lse=True, want_mass=True)
     torch.cuda.synchronize()
     for h in range(w.heads):
-        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group])
         ro, rl = O.causal_attention(qh, kh, vh)
         assert_attn_close(f64(o[0, h]), ro, w.dtype, f"{name} head {h} O")
         assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} head {h}")
@@ -66,7 +66,7 @@ def _oracle_masses(name, steps=(9, 10, 11, 12)):
     for si, t in enumerate(steps):
         q, k, _ = g.step_torch(t)
         for h in range(w.heads):
-            out[si, h] = O.block_mass(f64(q[0, h]), f64(k[0, h]))
+            out[si, h] = O.block_mass(f64(q[0, h]), f64(k[0, h // w.group]))
     return out
 
 
@@ -132,7 +132,8 @@ def test_sparse_attention_on_oracle_schedule(name):
         o, lse = wise.sparse_attn(*dev, sched, want_lse=True)
         torch.cuda.synchronize()
         for h in range(w.heads):
-            ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), rows[h * w.nq:(h + 1) * w.nq])
+            ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]),
+                                        rows[h * w.nq:(h + 1) * w.nq])
             assert_attn_close(f64(o[0, h]), ro, w.dtype, f"{name} step {t} head {h} O")
             assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} step {t} head {h}")
 
@@ -167,7 +168,8 @@ def test_end_to_end_trajectory(name):
     o, lse = wise.sparse_attn(*dev, sched, want_lse=True)
     torch.cuda.synchronize()
     for h in range(w.heads):
-        ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), ref_rows[h * w.nq:(h + 1) * w.nq])
+        ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]),
+                                    ref_rows[h * w.nq:(h + 1) * w.nq])
         keep = np.zeros(w.seqlen, dtype=bool)
         for r in same:
             if r // w.nq == h:
@@ -195,21 +197,23 @@ def test_eta_one_sparse_equals_dense(name):
     assert_attn_close(f64(os_), f64(od), w.dtype, "sparse(eta=1) vs dense")
     assert float((ls - ld).abs().max()) <= 1e-5
     for h in range(w.heads):
-        ro, _ = O.causal_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]))
+        ro, _ = O.causal_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]))
         assert_attn_close(f64(os_[0, h]), ro, w.dtype, "sparse(eta=1) vs oracle full")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("batch,heads,n", [(1, 1, 32), (2, 3, 96), (1, 2, 160)])
-def test_shapes_batch_and_head_dim(dtype, d, batch, heads, n):
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("batch,heads,kv,n", [(1, 1, 1, 32), (2, 3, 3, 96), (1, 2, 2, 160), (2, 4, 2, 96),
+                                               (1, 6, 1, 64)])
+def test_shapes_batch_and_head_dim(dtype, d, batch, heads, kv, n):
     wise = _wise()
     rng = np.random.default_rng(batch * 100 + heads * 10 + n + d)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    mk = lambda s: torch.from_numpy(rng.standard_normal((batch, heads, n, d)).astype(np.float32) * s).to(tdt)
-    q, k, v = mk(1.5), mk(1.5), mk(1.0)
+    mk = lambda hh, s: torch.from_numpy(rng.standard_normal((batch, hh, n, d)).astype(np.float32) * s).to(tdt)
+    q, k, v = mk(heads, 1.5), mk(kv, 1.5), mk(kv, 1.0)
+    grp = heads // kv
     nq = n // 32
-    note(f"shapes {dtype} d={d} b={batch} h={heads} n={n}")
+    note(f"shapes {dtype} d={d} b={batch} h={heads} kv={kv} n={n}")
     o, lse, mass = wise.full_attn_mass(q.to(DEV), k.to(DEV), v.to(DEV), want_lse=True, want_mass=True)
     rows = []
     for bb in range(batch):
@@ -221,7 +225,7 @@ def test_shapes_batch_and_head_dim(dtype, d, batch, heads, n):
     torch.cuda.synchronize()
     for bb in range(batch):
         for h in range(heads):
-            qh, kh, vh = f64(q[bb, h]), f64(k[bb, h]), f64(v[bb, h])
+            qh, kh, vh = f64(q[bb, h]), f64(k[bb, h // grp]), f64(v[bb, h // grp])
             ro, rl = O.causal_attention(qh, kh, vh)
             assert_attn_close(f64(o[bb, h]), ro, dtype, "dense O")
             assert_lse_close(f64(lse[bb, h]), rl, dtype, "dense")

@@ -26,9 +26,9 @@ def test_generator_is_deterministic_and_head_local():
 def test_drift_shrinks_with_step_and_steps_differ():
     w = S.WORKLOADS["tiny"]
     g = S.Generator(w)
-    base = g.base[0]
-    d1 = np.abs(g.step_f32(1)[0][0] - base[0]).std()
-    d32 = np.abs(g.step_f32(32)[0][0] - base[0]).std()
+    base = g.base_q[0]
+    d1 = np.abs(g.step_f32(1)[0][0] - base).std()
+    d32 = np.abs(g.step_f32(32)[0][0] - base).std()
     assert 0.02 < d1 < 0.08 and d32 < d1 / 10
     with pytest.raises(ValueError):
         g.step_f32(0)
@@ -72,3 +72,21 @@ def test_traffic_record_is_tied_to_the_kernel_source():
     t = bench.measured_traffic("4k")
     assert t is None or t > 1e8
     assert bench.measured_traffic("16k") is None
+
+
+def test_grouped_query_workload_shares_key_value_heads():
+    w = S.WORKLOADS["gqa"]
+    assert w.group == 4 and w.kvh == 2
+    q, k, v = S.Generator(w).step_f32(3)
+    assert q.shape[0] == 8 and k.shape[0] == 2 and v.shape[0] == 2
+    # a head subset carries the key-value heads its query heads read, in order of first use
+    qs, ks, vs = S.Generator(w, heads=[5, 1]).step_f32(3)
+    np.testing.assert_array_equal(qs[0], q[5])
+    np.testing.assert_array_equal(ks[0], k[1])
+    np.testing.assert_array_equal(ks[1], k[0])
+    # with one key-value head per query head the recipe is the plain one
+    p = S.WORKLOADS["1k"]
+    a = S.Generator(p, heads=[2]).step_f32(4)
+    b = S.drift_head(p, 2, 4, S.base_head(p, 2))
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x[0], y)
