@@ -138,9 +138,10 @@ def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
 
 def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
     """Untimed-trajectory extras (the WISE paper, App. B): retained future mass of
-    the WISE schedule at late steps, and the intervention-control schedules
-    (Static-95, SizeMatched, MassMatched from step-1 masses): density, retained
-    future mass, build time and sparse-step time on each."""
+    the WISE schedule at late steps; the intervention-control schedules
+    (Static-95, SizeMatched, MassMatched from step-1 masses) and the schedules
+    selected at block sizes 64 and 128 (Table 8): density, retained future mass,
+    build time and sparse-step time on each."""
     import torch
     bh, nq = w.batch * w.heads, w.nq
     out = torch.empty_like(steps[1][0])
@@ -176,6 +177,17 @@ def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
             "block_density": round(int(ctl.nnz.item()) / causal, 5),
             "retained_future_mass": {"t32": retained(ctl, 32)},
             "build_ms": round(build_ms, 4), "sparse_step_ms": round(sparse_ms, 4)}
+    if nq % 4 == 0:
+        for block in (64, 128):
+            blk = wise.alloc_schedule(bh, nq, mass.device)
+            wsb = torch.empty(int(wise.lib.wise_build_support_blocked_workspace_bytes(bh, nq, 4, block)),
+                              dtype=torch.uint8, device=mass.device)
+            build_ms = timed(lambda: wise.build_support(mass, eta, schedule=blk, workspace=wsb, block=block))
+            sparse_ms = timed(lambda: wise.sparse_attn(*steps[32], blk, out=out))
+            res[f"block{block}"] = {
+                "block_density": round(int(blk.nnz.item()) / causal, 5),
+                "retained_future_mass": {"t32": retained(blk, 32)},
+                "build_ms": round(build_ms, 4), "sparse_step_ms": round(sparse_ms, 4)}
     return res
 
 

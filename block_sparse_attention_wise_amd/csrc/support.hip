@@ -392,6 +392,36 @@ hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t
   return hipGetLastError();
 }
 
+// CSR (row_ptr, col_idx, nnz) and, if plan != null, the execution plan from the
+// per-row bitmasks and counts in the workspace
+static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz, int32_t* plan,
+                                  void* workspace, hipStream_t stream) {
+  const size_t rows = (size_t)bh * nq;
+  const int nwords = (nq + 31) / 32;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  uint32_t* masks = static_cast<uint32_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4));
+  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, (int)rows, row_ptr, nnz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, masks, nwords, row_ptr, col_idx);
+  e = hipGetLastError();
+  if (e != hipSuccess || plan == nullptr) return e;
+  // execution plan: plan[0..groups] = entry offsets, entries follow
+  const int ngroups = (nq + kPlanRows - 1) / kPlanRows;
+  const int groups = bh * ngroups;
+  int32_t* gcounts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4) + al(rows * 4));
+  hipLaunchKernelGGL(group_count_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, ngroups, gcounts);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, gcounts, groups, plan, plan + groups);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, ngroups, plan,
+                     plan + groups + 1);
+  return hipGetLastError();
+}
+
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
                           const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
                           int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream) {
@@ -414,25 +444,105 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, a.counts, (int)rows, row_ptr, nnz);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
+}
+
+// ---------------------------------------------------------------- coarser blocks
+//
+// Selection at block size B = 32 f (f = 2, 4) on the 32-token masses: the B-level
+// mass of Eq. 5 is (32 / B) times the sum of the f x f 32-level masses it covers
+// (Eq. 5 is linear in the attention weights), the cumulative-eta support and the
+// union run on those, and each 32-token query block then lists the 32-token key
+// blocks of its B-block's selected blocks that are causally admissible: the same
+// keys the B-level reuse mask admits, as the physical 32 x 32 tiles the sparse
+// kernel visits (the WISE paper, App. B, block-size study).
+
+// massB[t][bh][Q][b] for b <= Q (0 above), accumulated in fp64
+__global__ __launch_bounds__(kSelThreads) void aggregate_mass_kernel(const float* mass, int nq, int f, float* massB) {
+  const int nqb = nq / f;
+  const int row = blockIdx.x;  // (t * bh + bh_index) * nqb + Q
+  const int Q = row % nqb;
+  const size_t tb = (size_t)(row / nqb);
+  const float* src = mass + (tb * nq + (size_t)Q * f) * (size_t)nq;
+  float* dst = massB + (tb * nqb + Q) * (size_t)nqb;
+  for (int b = threadIdx.x; b < nqb; b += kSelThreads) {
+    double acc = 0.0;
+    if (b <= Q)
+      for (int qi = 0; qi < f; ++qi)
+        for (int ki = 0; ki < f; ++ki) acc += (double)src[(size_t)qi * nq + b * f + ki];
+    dst[b] = (float)(acc / f);
+  }
+}
+
+// 32-level row masks (and popcounts) from the B-level unions
+__global__ __launch_bounds__(64) void expand_masks_kernel(const uint32_t* masksB, int nqb, int nwordsB, int f, int nq,
+                                                          int nwords, uint32_t* masks, int32_t* counts) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const int bh = row / nq, q = row - bh * nq, Q = q / f;
+  const uint32_t* mb = masksB + (size_t)(bh * nqb + Q) * nwordsB;
+  int c = 0;
+  for (int w = lane; w < nwords; w += 64) {
+    uint32_t bits = 0u;
+    for (int j = 0; j < 32; ++j) {
+      const int k = 32 * w + j;
+      const int b = k / f;
+      if (k <= q && ((mb[b >> 5] >> (b & 31)) & 1u)) bits |= 1u << j;
+    }
+    masks[(size_t)row * nwords + w] = bits;
+    c += __popc(bits);
+  }
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if (lane == 0) counts[row] = c;
+}
+
+size_t support_blocked_workspace_bytes(int bh, int nq, int steps, int f) {
+  const size_t nqb = (size_t)nq / f;
+  const size_t nwb = (nqb + 31) / 32;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return support_workspace_bytes(bh, nq) + al((size_t)steps * bh * nqb * nqb * 4) + al((size_t)bh * nqb * nwb * 4) +
+         al((size_t)bh * nqb * 4);
+}
+
+hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, double eta, int f, int32_t* row_ptr,
+                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace,
+                                  hipStream_t stream) {
+  const int nqb = nq / f;
+  const int nwb = (nqb + 31) / 32;
+  const int nwords = (nq + 31) / 32;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* extra = static_cast<char*>(workspace) + support_workspace_bytes(bh, nq);
+  float* massB = reinterpret_cast<float*>(extra);
+  uint32_t* masksB = reinterpret_cast<uint32_t*>(extra + al((size_t)steps * bh * nqb * nqb * 4));
+  int32_t* countsB = reinterpret_cast<int32_t*>(extra + al((size_t)steps * bh * nqb * nqb * 4) +
+                                                al((size_t)bh * nqb * nwb * 4));
+  hipLaunchKernelGGL(aggregate_mass_kernel, dim3((unsigned)((size_t)steps * bh * nqb)), dim3(kSelThreads), 0, stream,
+                     mass, nq, f, massB);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SupportArgs a;
+  a.mass = massB;
+  a.bh = bh;
+  a.nq = nqb;
+  a.steps = steps;
+  a.eta = eta;
+  a.masks = masksB;
+  a.counts = countsB;
+  a.nwords = nwb;
+  a.kind = kCumulative;
+  a.ref_row_ptr = nullptr;
+  a.ref_col_idx = nullptr;
+  a.ref_cap = 0;
+  hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)((size_t)bh * nqb)), dim3(kSelThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.masks, nwords, row_ptr, col_idx);
-  e = hipGetLastError();
-  if (e != hipSuccess || plan == nullptr) return e;
-  // execution plan: plan[0..groups] = entry offsets, entries follow
-  const int ngroups = (nq + kPlanRows - 1) / kPlanRows;
-  const int groups = bh * ngroups;
-  int32_t* gcounts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4) + al(rows * 4));
-  hipLaunchKernelGGL(group_count_kernel, dim3(groups), dim3(64), 0, stream, a.masks, nq, nwords, ngroups, gcounts);
+  const size_t rows = (size_t)bh * nq;
+  uint32_t* masks = static_cast<uint32_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4));
+  hipLaunchKernelGGL(expand_masks_kernel, dim3((unsigned)rows), dim3(64), 0, stream, masksB, nqb, nwb, f, nq, nwords,
+                     masks, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, gcounts, groups, plan, plan + groups);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, a.masks, nq, nwords, ngroups, plan,
-                     plan + groups + 1);
-  return hipGetLastError();
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
 }
 
 }  // namespace wise

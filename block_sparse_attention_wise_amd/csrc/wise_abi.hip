@@ -62,9 +62,10 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seql
 }
 
 // checks shared by the schedule builders
+// workspace_need: bytes of workspace the builder needs (0: the plain builder's)
 wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_t* row_ptr, int32_t* col_idx,
                         int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity, void* workspace,
-                        size_t workspace_bytes) {
+                        size_t workspace_bytes, size_t workspace_need = 0) {
   if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
   if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
   if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
@@ -72,7 +73,7 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
   const int64_t worst = (int64_t)bh * nq * (nq + 1) / 2;
   if (worst > INT32_MAX) return WISE_ERR_INVALID_ARG;
   if (col_capacity < worst) return WISE_ERR_INVALID_ARG;
-  if (workspace_bytes < support_workspace_bytes(bh, nq)) return WISE_ERR_INVALID_ARG;
+  if (workspace_bytes < (workspace_need ? workspace_need : support_workspace_bytes(bh, nq))) return WISE_ERR_INVALID_ARG;
   if (plan != nullptr) {
     const size_t need = wise_build_support_plan_capacity(bh, nq);
     if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
@@ -137,6 +138,36 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, 0, nullptr, nullptr, 0, row_ptr, col_idx, nnz,
                                 plan, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
+}
+
+size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps, int block) {
+  if (block == kBlock) return wise_build_support_workspace_bytes(bh, nq, num_steps);
+  if (block != 2 * kBlock && block != 4 * kBlock) return 0;
+  const int f = block / kBlock;
+  if (bh <= 0 || nq <= 0 || nq > 4096 || nq % f != 0 || num_steps <= 0 || num_steps > 64) return 0;
+  if ((int64_t)bh * nq > INT32_MAX) return 0;
+  return support_blocked_workspace_bytes(bh, nq, num_steps, f);
+}
+
+wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps, const float* mass, float eta,
+                                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
+                                       int32_t* plan, int64_t plan_capacity, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (block == kBlock)
+    return wise_build_support(bh, nq, num_steps, mass, eta, row_ptr, col_idx, col_capacity, nnz, plan,
+                              plan_capacity, workspace, workspace_bytes, stream);
+  if (block != 2 * kBlock && block != 4 * kBlock) return WISE_ERR_UNSUPPORTED;
+  const int f = block / kBlock;
+  if (nq <= 0 || nq % f != 0) return WISE_ERR_INVALID_ARG;
+  const size_t need = wise_build_support_blocked_workspace_bytes(bh, nq, num_steps, block);
+  if (need == 0) return WISE_ERR_INVALID_ARG;
+  wise_status st = check_build(bh, nq, num_steps, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
+                               workspace, workspace_bytes, need);
+  if (st != WISE_OK) return st;
+  if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
+  hipError_t e = launch_support_blocked(mass, bh, nq, num_steps, (double)eta, f, row_ptr, col_idx, nnz, plan,
+                                        workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 

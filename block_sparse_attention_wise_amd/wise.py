@@ -19,11 +19,12 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_dense_attn",
     "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity", "wise_build_support",
     "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
+    "wise_build_support_blocked_workspace_bytes", "wise_build_support_blocked",
 )
 
 
@@ -47,6 +48,11 @@ def _load():
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
     lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.wise_build_support_blocked_workspace_bytes.restype = ctypes.c_size_t
+    lib.wise_build_support_blocked_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.wise_build_support_blocked.restype = i32
+    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp,
+                                               ctypes.c_size_t, vp]
     lib.wise_build_support_variant.restype = i32
     lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
                                                ctypes.c_size_t, vp]
@@ -196,8 +202,10 @@ def _plan_args(schedule: Schedule):
 
 
 def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspace=None, stream=None,
-                  with_plan: bool = True):
-    """Selection + temporal union + CSR (+ execution plan) from masses [num_steps, b*h, nq, nq] (fp32)."""
+                  with_plan: bool = True, block: int = BLOCK):
+    """Selection + temporal union + CSR (+ execution plan) from 32-token masses
+    [num_steps, b*h, nq, nq] (fp32).  block = 64 or 128 selects at that block size
+    (the schedule stays at 32-token granularity)."""
     if mass.dim() != 4 or mass.shape[2] != mass.shape[3]:
         raise ValueError("mass must be [num_steps, batch*heads, nq, nq]")
     if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
@@ -205,13 +213,15 @@ def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspa
     steps, bh, nq, _ = mass.shape
     if schedule is None:
         schedule = alloc_schedule(bh, nq, mass.device, with_plan=with_plan)
-    need = build_support_workspace_bytes(bh, nq, steps)
-    if workspace is None:
+    need = int(lib.wise_build_support_blocked_workspace_bytes(bh, nq, steps, block))
+    if need == 0:
+        raise ValueError(f"unsupported block size {block} for nq = {nq}")
+    if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=mass.device)
-    st = lib.wise_build_support(bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
-                                _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
-                                *_plan_args(schedule), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "wise_build_support")
+    st = lib.wise_build_support_blocked(block, bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
+                                        _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
+                                        *_plan_args(schedule), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "wise_build_support_blocked" if block != BLOCK else "wise_build_support")
     return schedule
 
 

@@ -53,7 +53,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 4
+#define WISE_ABI_VERSION 5
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -138,6 +138,29 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                int32_t* nnz, int32_t* plan, int64_t plan_capacity,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Working-set schedule selected at a coarser block size (the block-size study of
+ * the WISE paper, App. B, Table 8): block = 64 or 128 (32 falls through to
+ * wise_build_support).  The masses are the 32-token masses wise_full_attn_mass
+ * writes; the block-level mass of Eq. 5 at block B is (32/B) times the sum of
+ * the (B/32)^2 32-token masses it covers (Eq. 5 is linear in A), accumulated in
+ * fp64 and rounded to fp32.  The cumulative-eta support and the union over the
+ * steps are taken at block B; the output schedule (and plan) stays at the
+ * 32-token granularity the sparse kernel runs on: 32-token query block q lists
+ * every 32-token key block k <= q whose B-block is selected for q's B-block --
+ * exactly the keys the B-level reuse mask admits.
+ *   nq : 32-token query blocks; must be a multiple of block/32.
+ *   everything else as for wise_build_support, with
+ *   workspace_bytes >= wise_build_support_blocked_workspace_bytes(...).
+ * Other block sizes return WISE_ERR_UNSUPPORTED.
+ */
+size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps, int block);
+wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps, const float* mass,
+                                       float eta, int32_t* row_ptr, int32_t* col_idx,
+                                       int64_t col_capacity, int32_t* nnz, int32_t* plan,
+                                       int64_t plan_capacity, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /*
  * Intervention-control schedules of the WISE paper (App. B, intervention

@@ -5,7 +5,7 @@ the CPU-baseline leg of ``bench.py`` may use it; the HIP library never does.
 """
 from .wise_oracle import (  # noqa: F401
     attention_probs, block_density, block_mass, boundary_flags, build_csr,
-    causal_attention, mass_matched_support, retained_mass, scheduled_pairs,
+    causal_attention, expand_supports, mass_matched_support, retained_mass, scheduled_pairs,
     select_support, size_matched_support, sorted_order, sparse_attention,
     step_supports, union_supports,
 )

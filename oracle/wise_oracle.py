@@ -215,6 +215,24 @@ def union_supports(per_step):
     return out
 
 
+def expand_supports(supports, nq, block, tile=32):
+    """Supports selected at block size ``block`` (a multiple of ``tile``) as
+    per-``tile`` rows: tile query block q lists every tile key block k <= q whose
+    ``block``-sized key block is selected for q's ``block``-sized query block --
+    the keys the reuse mask of §5.2 admits at that block size, on the tile grid
+    (the WISE paper, App. B, block-size study).
+
+    supports: list over block-sized query blocks of index arrays; nq: tile-sized
+    query blocks.  Returns a list over tile query blocks of ascending arrays.
+    """
+    f = block // tile
+    out = []
+    for q in range(nq):
+        sel = set(int(b) for b in supports[q // f])
+        out.append(np.array([k for k in range(q + 1) if k // f in sel], dtype=np.int64))
+    return out
+
+
 def build_csr(supports):
     """CSR schedule of the WISE paper, App. B (sparse-kernel implementation): row
     offsets plus the active key-block indices of every (head, query block) row.

@@ -41,6 +41,10 @@ def lib():
     lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
                                                ctypes.c_size_t, vp]
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
+    lib.wise_build_support_blocked_workspace_bytes.restype = ctypes.c_size_t
+    lib.wise_build_support_blocked_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp,
+                                               ctypes.c_size_t, vp]
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
                                      f32, vp]
     lib.wise_status_string.restype = ctypes.c_char_p
@@ -53,13 +57,14 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) >= {"wise_full_attn_mass", "wise_dense_attn", "wise_build_support",
                           "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity",
                           "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
+                          "wise_build_support_blocked", "wise_build_support_blocked_workspace_bytes",
                           "wise_status_string", "wise_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in wise.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 4
+    assert lib.wise_abi_version() == 5
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -183,3 +188,25 @@ def test_variant_and_retained_validation(lib):
     for kw in (dict(mass=NULL), dict(rp=NULL), dict(ci=NULL), dict(out=NULL), dict(cap_=-1),
                dict(out=ctypes.c_void_p(0x20002))):
         assert ret(**kw) == INVALID, kw
+
+
+def test_blocked_builder_validation(lib):
+    f = lib.wise_build_support_blocked_workspace_bytes
+    al = lambda x: (x + 255) // 256 * 256
+    for bh, nq, steps, blk in ((2, 8, 4, 64), (3, 32, 4, 128), (1, 128, 1, 64)):
+        fct = blk // 32
+        nqb = nq // fct
+        base = al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4) + al(bh * ((nq + 3) // 4) * 4)
+        extra = al(steps * bh * nqb * nqb * 4) + al(bh * nqb * ((nqb + 31) // 32) * 4) + al(bh * nqb * 4)
+        assert f(bh, nq, steps, blk) == base + extra
+    assert f(2, 8, 4, 32) == lib.wise_build_support_workspace_bytes(2, 8, 4)
+    assert f(2, 8, 4, 48) == 0 and f(2, 9, 4, 64) == 0 and f(2, 8, 4, 16) == 0
+
+    def blk(block=64, bh=2, nq=8, steps=4, eta=0.95, cap=None, ws=P2, wsb=None):
+        cap = bh * nq * (nq + 1) // 2 if cap is None else cap
+        wsb = (f(bh, nq, steps, block) or 1 << 20) if wsb is None else wsb
+        return lib.wise_build_support_blocked(block, bh, nq, steps, P, eta, P, P, cap, P, NULL, 0, ws, wsb, None)
+    assert blk(block=48) == UNSUPPORTED and blk(block=16) == UNSUPPORTED
+    assert blk(nq=9) == INVALID                 # not a whole number of 64-token blocks
+    assert blk(wsb=f(2, 8, 4, 64) - 1) == INVALID
+    assert blk(eta=0.0) == INVALID and blk(cap=10) == INVALID
