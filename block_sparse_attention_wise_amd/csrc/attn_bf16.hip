@@ -184,17 +184,23 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
   const float m_use = st.m;
   // Block n's probabilities, then its P V products; the compiler overlaps
   // block n's MFMAs with block n + 1's exponentials.  The row sum is taken over
-  // the fp32 probabilities (the log-sum-exp feeds the block masses).
-  float lsum[16];
+  // the fp32 probabilities (the log-sum-exp feeds the block masses), reduced
+  // per block before its products so the probabilities die early.
+  float lsum = 0.f;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     bf16x8 pb[2];
+    float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(fmaf(s[n][r], sl2, -m_use));
-      pb[r >> 3][r & 7] = (__bf16)p;
-      lsum[r] = n == 0 ? p : lsum[r] + p;
+      p[r] = fast_exp2(fmaf(s[n][r], sl2, -m_use));
+      pb[r >> 3][r & 7] = (__bf16)p[r];
     }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[r] += p[r + 8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] += p[r + 4];
+    lsum += (p[0] + p[2]) + (p[1] + p[3]);
 #pragma unroll
     for (int t = 0; t < T::NT; ++t)
 #pragma unroll
@@ -202,11 +208,7 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
         st.acc[t] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], t, c2, lane), pb[c2], st.acc[t], 0, 0, 0);
   }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) lsum[r] += lsum[r + 8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) lsum[r] += lsum[r + 4];
-  st.l += (lsum[0] + lsum[2]) + (lsum[1] + lsum[3]);
+  st.l += lsum;
 }
 
 // Normalise and store O (bf16) and the natural-log LSE of one query block.
@@ -332,7 +334,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   __shared__ __attribute__((aligned(16))) __bf16 vt[TRIP][32 * T::VSTRIDE];
   __shared__ uint32_t rmask[SPARSE ? W * kMaxMaskWords : 1];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // uniform per wavefront (the compiler cannot tell that tid >> 6 is)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 31, h = lane >> 5;
   const int ngroups = (a.nq + W - 1) / W;
   const int bhn = a.rows / a.nq;
