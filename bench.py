@@ -140,8 +140,8 @@ def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
     """Untimed-trajectory extras (the WISE paper, App. B): retained future mass of
     the WISE schedule at late steps; the intervention-control schedules
     (Static-95, SizeMatched, MassMatched from step-1 masses) and the schedules
-    selected at block sizes 64 and 128 (Table 8): density, retained future mass,
-    build time and sparse-step time on each."""
+    selected at block sizes 16, 64 and 128 (Table 8): density, retained future
+    mass, build time and sparse-step time on each."""
     import torch
     bh, nq = w.batch * w.heads, w.nq
     out = torch.empty_like(steps[1][0])
@@ -188,6 +188,27 @@ def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
                 "block_density": round(int(blk.nnz.item()) / causal, 5),
                 "retained_future_mass": {"t32": retained(blk, 32)},
                 "build_ms": round(build_ms, 4), "sparse_step_ms": round(sparse_ms, 4)}
+    if 2 * nq <= 2048:
+        # B = 16: 16-token masses from the discovery kernel, the plain builder on
+        # them, the sparse step over the 16-token CSR; density is reported over the
+        # 16-token causal block pairs, retained mass against 16-token future masses
+        n16 = 2 * nq
+        m16 = torch.empty((4, bh, n16, n16), dtype=torch.float32, device=mass.device)
+        disc_ms = timed(lambda: [wise.full_attn_mass(*steps[t], out=out, mass=m16[i], block=16)
+                                 for i, t in enumerate((9, 10, 11, 12))])
+        blk = wise.alloc_schedule(bh, n16, mass.device, with_plan=False)
+        ws16 = torch.empty(int(wise.build_support_workspace_bytes(bh, n16, 4)), dtype=torch.uint8,
+                           device=mass.device)
+        build_ms = timed(lambda: wise.build_support(m16, eta, schedule=blk, workspace=ws16, with_plan=False))
+        sparse_ms = timed(lambda: wise.sparse_attn(*steps[32], blk, out=out, block=16))
+        late16 = torch.empty((bh, n16, n16), dtype=torch.float32, device=mass.device)
+        wise.full_attn_mass(*steps[32], out=out, mass=late16, block=16)
+        r = wise.retained_mass(late16, blk).cpu().numpy()
+        res["block16"] = {
+            "block_density": round(int(blk.nnz.item()) / (bh * n16 * (n16 + 1) // 2), 5),
+            "retained_future_mass": {"t32": {"mean": round(float(r.mean()), 5), "min": round(float(r.min()), 5)}},
+            "discovery_mass_ms_4_steps": round(disc_ms, 4),
+            "build_ms": round(build_ms, 4), "sparse_step_ms": round(sparse_ms, 4)}
     return res
 
 

@@ -135,10 +135,14 @@ __device__ __forceinline__ float max_tree3(const float (&v)[K]) {
 // softmax work between dependent instructions, and halve the max/rescale work
 // per block.  The K fragments are read from the LDS tiles kt[n] (row i, this
 // lane's half), the V^T operands from vt[n].
-template <int D, int N, class QS>
+// SUB (16-token blocks on the 32 x 32 tiles): bits 4n..4n+3 of sub_bits say which
+// 16 x 16 sub-blocks of tile n are scheduled (bit 2 qh + kh: query half qh, key
+// half kh); keys of unscheduled sub-blocks are masked like non-causal ones, and
+// a query half with no key yet keeps l = 0 and O = 0.
+template <int D, int N, class QS, bool SUB = false>
 __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* const (&kt)[N], const QS& qf,
                                              const __bf16* const (&vt)[N], const bool (&diag)[N], int i, int h,
-                                             int lane, float sl2) {
+                                             int lane, float sl2, int sub_bits = 0xFF) {
   using T = Tile<D>;
   floatx16 s[N];
 #pragma unroll
@@ -162,6 +166,16 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
       for (int r = 0; r < 16; ++r)
         if (acc_row(r, h) > i) s[n][r] = -INFINITY;
     }
+    if (SUB) {
+      const int sb = (sub_bits >> (4 * n)) & 0xF;
+      if (sb != 0xF) {
+        // registers 0..7 hold keys 0..15 of the tile, 8..15 keys 16..31
+        const int ml = (sb >> (2 * (i >> 4))) & 3;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((ml >> (r >> 3)) & 1)) s[n][r] = -INFINITY;
+      }
+    }
   }
   float all[16 * N];
 #pragma unroll
@@ -175,13 +189,13 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
   // kSlack; otherwise p <= 2^kSlack, exact in fp32 and fine for bf16 P.
   if (__ballot(tmax > st.m + kSlack) != 0ull) {
     const float m_new = fmaxf(st.m, tmax);
-    const float alpha = fast_exp2(st.m - m_new);
+    const float alpha = SUB && m_new == -INFINITY ? 1.f : fast_exp2(st.m - m_new);
     st.l *= alpha;
 #pragma unroll
     for (int t = 0; t < T::NT; ++t) st.acc[t] *= alpha;
     st.m = m_new;
   }
-  const float m_use = st.m;
+  const float m_use = SUB && st.m == -INFINITY ? 0.f : st.m;
   // Block n's probabilities, then its P V products; the compiler overlaps
   // block n's MFMAs with block n + 1's exponentials.  The row sum is taken over
   // the fp32 probabilities (the log-sum-exp feeds the block masses), reduced
@@ -241,7 +255,11 @@ __device__ __forceinline__ float finish_rows(const RowState<D>& st, __bf16* orow
 //   dense   (W = 4, TRIP = 2) list = 0 .. q0+3, wavefront w takes b <= q0 + w;
 //   sparse  (W = 4, TRIP = 4) list = union of the 4 rows' scheduled blocks (the
 //           execution plan's order, else ascending), wavefront w takes the
-//           blocks of its own row.
+//           blocks of its own row;
+//   16-token blocks: a wavefront's 32 queries are two 16-token query blocks; the
+//           block mass is summed per 16 x 16 sub-block of each tile, and the
+//           sparse list walks the 32-key tiles holding any scheduled 16-token key
+//           block of the two rows, masking the unscheduled sub-blocks.
 // Neighbouring query blocks share key blocks (the sink, recent context), so the
 // sparse union reads each shared block once per workgroup.  Global loads run one
 // trip ahead of the compute through register staging sets.
@@ -251,9 +269,11 @@ constexpr int kSparseWaves = kPlanRows;  // sparse workgroups
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left free
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 constexpr int kMaxMaskWords = 128;  // sparse rows: nq <= 4096
+constexpr int kSubWords = 64;       // 16-token sparse rows: 2 * nq <= 2048
 constexpr int kEntryShift = 8;      // list entries: (block << 8) | row mask
 
-enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2 };
+// kDenseMass16 / kSparse16: the block mass and the schedule at 16-token blocks
+enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2, kDenseMass16 = 3, kSparse16 = 4 };
 constexpr int kSparseTrip = kPlanTrip;  // tiles per trip of the sparse kernel
 
 // Key-block lists.  next() is wave-uniform (scalar) control flow and returns an
@@ -320,7 +340,9 @@ struct PlanList {
 template <int D, int MODE>
 __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   using T = Tile<D>;
-  constexpr bool SPARSE = MODE == kSparse;
+  constexpr bool SPARSE = MODE == kSparse || MODE == kSparse16;
+  constexpr bool SUB = MODE == kSparse16;
+  constexpr bool MASS = MODE == kDenseMass || MODE == kDenseMass16;
   constexpr int W = SPARSE ? kSparseWaves : kWaves;  // wavefronts = query blocks per workgroup
   constexpr int NTHR = 64 * W;
   constexpr int CHUNKS = 32 * T::C8;                // 16-byte chunks of one tile
@@ -333,6 +355,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   __shared__ __attribute__((aligned(16))) __bf16 kt[TRIP][32 * T::KSTRIDE];
   __shared__ __attribute__((aligned(16))) __bf16 vt[TRIP][32 * T::VSTRIDE];
   __shared__ uint32_t rmask[SPARSE ? W * kMaxMaskWords : 1];
+  __shared__ uint32_t smask[SUB ? W * 2 * kSubWords : 1];  // the two 16-token rows of each wavefront
 
   const int tid = threadIdx.x, lane = tid & 63;
   // uniform per wavefront (the compiler cannot tell that tid >> 6 is)
@@ -367,16 +390,37 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * min(qb, a.nq - 1) + i) * D, h);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-  if (SPARSE && a.plan == nullptr) {
+  if (SPARSE && (a.plan == nullptr || SUB)) {
     // this wavefront's row as a bitmask over key blocks (entries outside 0..qb
     // and offsets outside 0..col_cap are ignored; duplicates count once)
     const int nwords = (qlast >> 5) + 1;
     uint32_t* my = rmask + wave * kMaxMaskWords;
     for (int w = lane; w < nwords; w += 64) my[w] = 0u;
+    if (SUB)
+      for (int w = lane; w < 2 * kSubWords; w += 64) smask[wave * 2 * kSubWords + w] = 0u;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (active) {
+    if (SUB && active) {
+      // 16-token rows 2 qb and 2 qb + 1 (key blocks 0 .. their own index): each
+      // scheduled 16-token block sets its bit in the row's mask and its tile's
+      // bit in the wavefront's tile mask
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int q16 = 2 * qb + x, row = bh * 2 * a.nq + q16;
+        uint32_t* sm = smask + (wave * 2 + x) * kSubWords;
+        int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
+        b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
+        b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
+        for (int64_t e = b0 + lane; e < b1; e += 64) {
+          const int b = a.col_idx[e];
+          if (b >= 0 && b <= q16) {
+            atomicOr(&sm[b >> 5], 1u << (b & 31));
+            atomicOr(&my[b >> 6], 1u << ((b >> 1) & 31));
+          }
+        }
+      }
+    } else if (active) {
       const int row = bh * a.nq + qb;
       int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
       b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
@@ -454,6 +498,15 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   RowState<D> st;
   st.init();
   // a trip's tiles of this wavefront's row, two per softmax step
+  // 16-token blocks: which 16 x 16 sub-blocks of tile b this wavefront's two rows
+  // schedule (bit 2 x + kh: row 2 qb + x, key block 2 b + kh)
+  auto sub4 = [&](int b) -> int {
+    if (!SUB) return 0xF;
+    const uint32_t* sm = smask + wave * 2 * kSubWords + ((2 * b) >> 5);
+    const int sh = (2 * b) & 31;
+    return (int)((__builtin_amdgcn_readfirstlane(sm[0]) >> sh) & 3u) |
+           (int)(((__builtin_amdgcn_readfirstlane(sm[kSubWords]) >> sh) & 3u) << 2);
+  };
   auto attend = [&](const int (&c)[TRIP]) {
     int mine = 0, dg = 0;
 #pragma unroll
@@ -469,7 +522,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const __bf16* const kp[2] = {kt[u0], kt[u1]};
       const __bf16* const vp[2] = {vt[u0], vt[u1]};
       const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
-      attend_tiles<D, 2>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2);
+      attend_tiles<D, 2, QRegs<D>, SUB>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
+                                        sub4(c[u0] >> kEntryShift) | (sub4(c[u1] >> kEntryShift) << 4));
     }
     while (mine) {
       const int u0 = __builtin_ctz(mine);
@@ -477,10 +531,11 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const __bf16* const kp[1] = {kt[u0]};
       const __bf16* const vp[1] = {vt[u0]};
       const bool dp[1] = {((dg >> u0) & 1) != 0};
-      attend_tiles<D, 1>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2);
+      attend_tiles<D, 1, QRegs<D>, SUB>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
+                                        sub4(c[u0] >> kEntryShift) | 0xF0);
     }
   };
-  if (SPARSE && a.plan != nullptr) {
+  if (SPARSE && !SUB && a.plan != nullptr) {
     const int groups = bhn * ngroups, g = bh * ngroups + grp;
     const int64_t cap = a.plan_cap - groups - 1;  // readable entries after the offsets
     int64_t p0 = a.plan[g], p1 = a.plan[g + 1];
@@ -504,12 +559,16 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     lse2 = finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
   }
 
-  if (MODE == kDenseMass) {
-    // Block mass (Eq. 5): r_qb = (1/32) sum_i sum_{j in b, j <= i} exp(s_ij - lse_i),
+  if (MASS) {
+    // Block mass (Eq. 5): r_qb = (1/B) sum_i sum_{j in b, j <= i} exp(s_ij - lse_i),
     // a second sweep over the keys now that every row's log-sum-exp is final.
-    float* mrow = a.mass + (size_t)(bh * a.nq + qb) * a.nq;
-    DenseList list{0, qlast + 1};
-    stream(list, false, [&](const int (&c)[TRIP]) {
+    // B = 32: one value per tile; B = 16: one per 16 x 16 sub-block (registers
+    // 0..7 hold the tile's first 16 keys, lanes i < 16 its first 16 queries).
+    constexpr bool B16 = MODE == kDenseMass16;
+    const int nm = B16 ? 2 * a.nq : a.nq;  // mass row length
+    float* mrow = a.mass + (size_t)(bh * a.nq + qb) * (B16 ? 4 * a.nq : a.nq);
+    DenseList mlist{0, qlast + 1};
+    stream(mlist, false, [&](const int (&c)[TRIP]) {
 #pragma unroll
       for (int buf = 0; buf < TRIP; ++buf) {
         const int b = c[buf] >> kEntryShift;
@@ -517,19 +576,43 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
         bf16x8 kf[T::NC];
         load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
         floatx16 s = qk_tile<D>(kf, qf);
-        float part = 0.f;
+        float part[2] = {0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(s[r], a.scale_log2, -lse2));
           if (b == qb && acc_row(r, h) > i) p = 0.f;
-          part += p;
+          part[r >> 3] += p;
         }
-        const float tot = wave_sum(part);
-        if (lane == 0) mrow[b] = tot * (1.f / 32.f);
+        if (!B16) {
+          const float tot = wave_sum(part[0] + part[1]);
+          if (lane == 0) mrow[b] = tot * (1.f / 32.f);
+        } else {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            float x = part[kh];  // 16-lane row sums land in lanes 15, 31, 47, 63
+            x += row_shr<1>(x);
+            x += row_shr<2>(x);
+            x += row_shr<4>(x);
+            x += row_shr<8>(x);
+            const int xi = __float_as_int(x);
+            const float s0 = __int_as_float(__builtin_amdgcn_readlane(xi, 15)) +
+                             __int_as_float(__builtin_amdgcn_readlane(xi, 47));
+            const float s1 = __int_as_float(__builtin_amdgcn_readlane(xi, 31)) +
+                             __int_as_float(__builtin_amdgcn_readlane(xi, 63));
+            if (lane == 0) {
+              mrow[2 * b + kh] = s0 * (1.f / 16.f);       // query block 2 qb
+              mrow[nm + 2 * b + kh] = s1 * (1.f / 16.f);  // query block 2 qb + 1
+            }
+          }
+        }
       }
     });
-    if (active)
-      for (int b = qb + 1 + lane; b < a.nq; b += 64) mrow[b] = 0.f;
+    if (active) {
+      for (int b = (B16 ? 2 : 1) * (qb + 1) + lane; b < nm; b += 64) {
+        mrow[b] = 0.f;
+        if (B16) mrow[nm + b] = 0.f;
+      }
+    }
   }
 }
 
@@ -541,40 +624,43 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
     AttnBf16Args a) {
   attn_stream<D, MODE>(a);
 }
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(64 * kSparseWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sparse_kernel(
     AttnBf16Args a) {
-  attn_stream<D, kSparse>(a);
+  attn_stream<D, MODE>(a);
 }
 
 // ------------------------------------------------------------------ launch
 
-hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream) {
+template <int D>
+static void launch_d(const AttnBf16Args& a, bool sparse, bool mass, bool b16, hipStream_t stream) {
   const int bhn = a.rows / a.nq;
   const int w = sparse ? kSparseWaves : kWaves;
   const dim3 grid(bhn * ((a.nq + w - 1) / w)), block(64 * w);
-  if (head_dim == 96) {
-    if (sparse)
-      hipLaunchKernelGGL((attn_sparse_kernel<96>), grid, block, 0, stream, a);
-    else if (mass)
-      hipLaunchKernelGGL((attn_dense_kernel<96, kDenseMass>), grid, block, 0, stream, a);
+  if (sparse) {
+    if (b16)
+      hipLaunchKernelGGL((attn_sparse_kernel<D, kSparse16>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_dense_kernel<96, kDense>), grid, block, 0, stream, a);
-  } else if (head_dim == 128) {
-    if (sparse)
-      hipLaunchKernelGGL((attn_sparse_kernel<128>), grid, block, 0, stream, a);
-    else if (mass)
-      hipLaunchKernelGGL((attn_dense_kernel<128, kDenseMass>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_sparse_kernel<D, kSparse>), grid, block, 0, stream, a);
+  } else if (mass) {
+    if (b16)
+      hipLaunchKernelGGL((attn_dense_kernel<D, kDenseMass16>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_dense_kernel<128, kDense>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((attn_dense_kernel<D, kDenseMass>), grid, block, 0, stream, a);
   } else {
-    if (sparse)
-      hipLaunchKernelGGL((attn_sparse_kernel<64>), grid, block, 0, stream, a);
-    else if (mass)
-      hipLaunchKernelGGL((attn_dense_kernel<64, kDenseMass>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_dense_kernel<64, kDense>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_dense_kernel<D, kDense>), grid, block, 0, stream, a);
   }
+}
+
+// a.nq counts 32-query tiles; b16: masses and schedule at 16-token blocks
+hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, bool b16,
+                            hipStream_t stream) {
+  if (head_dim == 96)
+    launch_d<96>(a, sparse, mass, b16, stream);
+  else if (head_dim == 128)
+    launch_d<128>(a, sparse, mass, b16, stream);
+  else
+    launch_d<64>(a, sparse, mass, b16, stream);
   return hipGetLastError();
 }
 

@@ -8,6 +8,10 @@
 // One 256-thread workgroup owns one (batch*head, query block) row of 32 queries.
 // Q, K and V tiles are staged in LDS; thread t computes scores of query t/8
 // against keys 4*(t%8) .. +3, and output columns t%8 + 8*u of query t/8.
+// B16: 16-token blocks on the same 32 x 32 tiles -- the workgroup's queries are
+// two 16-token query blocks, the block mass is summed per 16 x 16 sub-block and
+// the sparse walk visits the 32-key tiles holding a scheduled 16-token key block
+// of either row, masking the unscheduled sub-blocks.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,7 +29,9 @@ __device__ __forceinline__ float group8_sum(float x) {
   return x + __shfl_xor(x, 4);
 }
 
-template <int D, bool SPARSE, bool MASS>
+constexpr int kSubWords32 = 64;  // 16-token sparse rows: 2 * nq <= 2048
+
+template <int D, bool SPARSE, bool MASS, bool B16>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   constexpr int S = D + 1;  // padded LDS stride (floats)
   constexpr int NU = D / 8;
@@ -34,6 +40,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   __shared__ float vs[32 * S];
   __shared__ float ps[32 * 33];
   __shared__ float red[8];
+  __shared__ uint32_t smask[B16 && SPARSE ? 2 * kSubWords32 : 1];  // the two 16-token rows
 
   const int tid = threadIdx.x;
   const int qi = tid >> 3, sub = tid & 7;
@@ -49,7 +56,23 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   for (int e = tid; e < 32 * D; e += 256) qs[(e / D) * S + e % D] = qh[e];
 
   int beg = 0, end = qb + 1;
-  if (SPARSE) {
+  if (SPARSE && B16) {
+    // rows 2 qb and 2 qb + 1 of the 16-token schedule as bitmasks (blocks
+    // 0 .. the row's own index); the walk below visits tiles 0..qb
+    for (int w = tid; w < 2 * kSubWords32; w += 256) smask[w] = 0u;
+    __syncthreads();
+    for (int x = 0; x < 2; ++x) {
+      const int q16 = 2 * qb + x, r16 = bh * 2 * a.nq + q16;
+      int64_t b0 = a.row_ptr[r16], b1 = a.row_ptr[r16 + 1];
+      b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
+      b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
+      for (int64_t e = b0 + tid; e < b1; e += 256) {
+        const int b = a.col_idx[e];
+        if (b >= 0 && b <= q16) atomicOr(&smask[x * kSubWords32 + (b >> 5)], 1u << (b & 31));
+      }
+    }
+    __syncthreads();
+  } else if (SPARSE) {
     int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
     b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
     b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
@@ -64,8 +87,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   const int qrow = 32 * qb + qi;
 
   for (int it = beg; it < end; ++it) {
-    const int b = SPARSE ? a.col_idx[it] : it;
-    if (SPARSE && (b < 0 || b > qb)) continue;
+    const int b = SPARSE && !B16 ? a.col_idx[it] : it;
+    if (SPARSE && !B16 && (b < 0 || b > qb)) continue;
+    // B16: which 16 x 16 sub-blocks of tile b are scheduled (bit 2 x + kh)
+    int subm = 0xF;
+    if (SPARSE && B16) {
+      const int sh = (2 * b) & 31;
+      subm = (int)((smask[(2 * b) >> 5] >> sh) & 3u) | (int)(((smask[kSubWords32 + ((2 * b) >> 5)] >> sh) & 3u) << 2);
+      if (subm == 0) continue;
+    }
     __syncthreads();
     const float* kb = a.k + kv_off + (size_t)(32 * b) * D;
     const float* vb = a.v + kv_off + (size_t)(32 * b) * D;
@@ -83,17 +113,19 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
       for (int d = 0; d < D; ++d) dot = fmaf(qs[qi * S + d], ks[j * S + d], dot);
       float x = dot * a.scale;
       if (32 * b + j > qrow) x = -INFINITY;
+      if (!((subm >> (2 * (qi >> 4) + (j >> 4))) & 1)) x = -INFINITY;
       sc[c] = x;
       mx = fmaxf(mx, x);
     }
     mx = group8_max(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = expf(m_run - m_new);
+    // a query half with no scheduled key yet (16-token blocks) keeps l = 0, O = 0
+    const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float p = expf(sc[c] - m_new);
+      const float p = sc[c] == -INFINITY ? 0.f : expf(sc[c] - m_new);
       ps[qi * 33 + 4 * sub + c] = p;
       psum += p;
     }
@@ -115,7 +147,40 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   const float lse = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
   if (a.lse != nullptr && sub == 0) a.lse[(size_t)bh * a.seqlen + qrow] = lse;
 
-  if (MASS) {
+  if (MASS && B16) {
+    // mass[2 qb + x][2 b + kh], x = query half (waves 0-1 / 2-3), kh = key half
+    const int nm = 2 * a.nq;
+    float* mrow = a.mass + (size_t)(bh * nm + 2 * qb) * nm;
+    for (int b = 0; b <= qb; ++b) {
+      __syncthreads();
+      const float* kb = a.k + kv_off + (size_t)(32 * b) * D;
+      for (int e = tid; e < 32 * D; e += 256) ks[(e / D) * S + e % D] = kb[e];
+      __syncthreads();
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * sub + c;
+        if (32 * b + j > qrow) continue;
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(qs[qi * S + d], ks[j * S + d], dot);
+        part += expf(dot * a.scale - lse);
+      }
+      const float p0 = wave_sum(sub < 4 ? part : 0.f), p1 = wave_sum(sub < 4 ? 0.f : part);
+      if ((tid & 63) == 0) {
+        red[2 * (tid >> 6)] = p0;
+        red[2 * (tid >> 6) + 1] = p1;
+      }
+      __syncthreads();
+      if (tid < 4) {
+        const int x = tid >> 1, kh = tid & 1;
+        mrow[x * nm + 2 * b + kh] = (red[4 * x + kh] + red[4 * x + 2 + kh]) * (1.f / 16.f);
+      }
+    }
+    for (int b = 2 * (qb + 1) + tid; b < nm; b += 256) {
+      mrow[b] = 0.f;
+      mrow[nm + b] = 0.f;
+    }
+  } else if (MASS) {
     float* mrow = a.mass + (size_t)row * a.nq;
     for (int b = 0; b <= qb; ++b) {
       __syncthreads();
@@ -140,23 +205,24 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   }
 }
 
-template <int D, bool SPARSE, bool MASS>
+template <int D, bool SPARSE, bool MASS, bool B16>
 static hipError_t launch(const AttnF32Args& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_f32_kernel<D, SPARSE, MASS>), dim3(a.rows), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_f32_kernel<D, SPARSE, MASS, B16>), dim3(a.rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream) {
-  if (head_dim == 128) {
-    if (sparse) return launch<128, true, false>(a, stream);
-    return mass ? launch<128, false, true>(a, stream) : launch<128, false, false>(a, stream);
-  }
-  if (head_dim == 96) {
-    if (sparse) return launch<96, true, false>(a, stream);
-    return mass ? launch<96, false, true>(a, stream) : launch<96, false, false>(a, stream);
-  }
-  if (sparse) return launch<64, true, false>(a, stream);
-  return mass ? launch<64, false, true>(a, stream) : launch<64, false, false>(a, stream);
+template <int D>
+static hipError_t launch_d(const AttnF32Args& a, bool sparse, bool mass, bool b16, hipStream_t stream) {
+  if (sparse) return b16 ? launch<D, true, false, true>(a, stream) : launch<D, true, false, false>(a, stream);
+  if (mass) return b16 ? launch<D, false, true, true>(a, stream) : launch<D, false, true, false>(a, stream);
+  return launch<D, false, false, false>(a, stream);
+}
+
+hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, bool b16,
+                           hipStream_t stream) {
+  if (head_dim == 128) return launch_d<128>(a, sparse, mass, b16, stream);
+  if (head_dim == 96) return launch_d<96>(a, sparse, mass, b16, stream);
+  return launch_d<64>(a, sparse, mass, b16, stream);
 }
 
 }  // namespace wise

@@ -50,8 +50,12 @@ struct AttnF32Args {
   float scale;               // softmax scale (natural-log units)
 };
 
-hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
-hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, hipStream_t stream);
+// nq in the argument structs counts 32-query tiles; b16 selects 16-token block
+// masses (mass [bh][2 nq][2 nq]) and 16-token schedules (rows bh * 2 nq)
+hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bool mass, bool b16,
+                            hipStream_t stream);
+hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, bool b16,
+                           hipStream_t stream);
 size_t support_workspace_bytes(int bh, int nq);
 size_t plan_capacity(int bh, int nq);
 // kind: 0 cumulative-eta support per step, unioned over the steps; 1 SizeMatched and

@@ -9,8 +9,9 @@
 namespace wise {
 namespace {
 
-constexpr int kBlock = 32;
-constexpr int kMaxSparseBlocks = 4096;  // bf16 sparse kernel: key blocks per row bitmask
+constexpr int kBlock = 32;              // the kernels' query and key tile
+constexpr int kMaxSparseBlocks = 4096;  // bf16 sparse kernel: key tiles per row bitmask
+constexpr int kMaxSparseBlocks16 = 2048;  // ... 16-token key blocks per row
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -26,8 +27,9 @@ wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int kv_heads, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WISE_ERR_INVALID_ARG;
   if (lse && !aligned4(lse)) return WISE_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return WISE_ERR_INVALID_ARG;
-  if (block != kBlock) return WISE_ERR_UNSUPPORTED;
+  if (block != kBlock && block != kBlock / 2) return WISE_ERR_UNSUPPORTED;
   if (seqlen % block != 0) return WISE_ERR_INVALID_ARG;
+  if (seqlen % kBlock != 0) return WISE_ERR_UNSUPPORTED;  // 16-token blocks still tile 32 queries
   if (head_dim != 64 && head_dim != 96 && head_dim != 128) return WISE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)batch * heads * (seqlen / block);
   const int64_t elems = (int64_t)batch * heads * seqlen * head_dim;
@@ -37,10 +39,11 @@ wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int kv_heads, 
 
 float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim); }
 
-wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, const void* q,
-                     const void* k, const void* v, void* o, float* lse, float* mass, const int32_t* row_ptr,
-                     const int32_t* col_idx, int64_t col_cap, const int32_t* plan, int64_t plan_cap, bool sparse,
-                     float scale, void* stream) {
+wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
+                     const void* q, const void* k, const void* v, void* o, float* lse, float* mass,
+                     const int32_t* row_ptr, const int32_t* col_idx, int64_t col_cap, const int32_t* plan,
+                     int64_t plan_cap, bool sparse, float scale, void* stream) {
+  const bool b16 = block == kBlock / 2;
   if (col_cap > INT32_MAX) col_cap = INT32_MAX;
   if (plan_cap > INT32_MAX) plan_cap = INT32_MAX;
   const int nq = seqlen / kBlock;
@@ -51,12 +54,12 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seql
     AttnBf16Args a{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
                    static_cast<__bf16*>(o), lse, mass, row_ptr, col_idx, col_cap, plan, plan_cap, seqlen, nq, rows,
                    heads, heads / kv_heads, sc * 1.4426950408889634f};
-    e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
+    e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, b16, static_cast<hipStream_t>(stream));
   } else {
     AttnF32Args a{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
                   static_cast<float*>(o), lse, mass, row_ptr, col_idx, col_cap, seqlen, nq, rows, heads,
                   heads / kv_heads, sc};
-    e = launch_attn_f32(a, head_dim, sparse, mass != nullptr, static_cast<hipStream_t>(stream));
+    e = launch_attn_f32(a, head_dim, sparse, mass != nullptr, b16, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
@@ -106,8 +109,8 @@ wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_head
   wise_status st = check_attn_shape(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
   if (st != WISE_OK) return st;
   if (mass && !aligned4(mass)) return WISE_ERR_INVALID_ARG;
-  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, q, k, v, o, lse, mass, nullptr, nullptr, 0, nullptr,
-                  0, false, scale, stream);
+  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, mass, nullptr, nullptr, 0,
+                  nullptr, 0, false, scale, stream);
 }
 
 wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
@@ -222,14 +225,15 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
   if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
   if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
   if (dt == WISE_BF16 && seqlen / kBlock > kMaxSparseBlocks) return WISE_ERR_UNSUPPORTED;
+  if (dt == WISE_BF16 && block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
   if (plan != nullptr) {
     const int64_t groups = (int64_t)batch * heads * ((seqlen / kBlock + kPlanRows - 1) / kPlanRows);
     if (!aligned4(plan) || plan_capacity < groups + 1) return WISE_ERR_INVALID_ARG;
-    if (dt != WISE_BF16) plan = nullptr;  // the fp32 kernel walks the CSR rows
+    // the fp32 kernel and 16-token schedules walk the CSR rows
+    if (dt != WISE_BF16 || block != kBlock) plan = nullptr;
   }
-  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, q, k, v, o, lse, nullptr, row_ptr, col_idx,
-                  col_capacity,
-                  plan, plan_capacity, true, scale, stream);
+  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, row_ptr, col_idx,
+                  col_capacity, plan, plan_capacity, true, scale, stream);
 }
 
 }  // extern "C"

@@ -133,7 +133,8 @@ def _f32_buf(t, numel, device, name):
 
 def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, want_mass=False,
                    scale=None, block=BLOCK, stream=None):
-    """Causal attention O (and optionally row LSE and block masses [b*h, nq, nq]).
+    """Causal attention O (and optionally row LSE and block masses [b*h, nq, nq],
+    nq = seqlen / block; block 32, or 16 for 16-token masses).
 
     Returns (out, lse, mass); lse / mass are None unless passed or requested.
     """
@@ -278,7 +279,8 @@ def retained_mass(mass, schedule: Schedule, *, out=None, stream=None):
 def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=False, scale=None,
                 block=BLOCK, stream=None):
     """Block-sparse causal attention over a CSR schedule (walking its execution plan when it
-    carries one).  Returns (out, lse)."""
+    carries one).  block 16 takes a 16-token schedule (build_support on 16-token masses;
+    no plan).  Returns (out, lse)."""
     b, h, hk, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     if want_lse and lse is None:

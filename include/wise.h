@@ -28,8 +28,12 @@
  *     argument nothing is launched and WISE_ERR_INVALID_ARG (or
  *     WISE_ERR_UNSUPPORTED for a valid but unimplemented shape) is returned.
  *     WISE_ERR_HIP reports a failed launch.
- *   - Only block = 32 and head_dim in {64, 96, 128} are implemented; seqlen must be
- *     a positive multiple of block.  scale <= 0 selects 1/sqrt(head_dim).
+ *   - block = 32, and block = 16 for the attention entry points (the block-size
+ *     study of the WISE paper, App. B, Table 8; the kernels still work on 32 x 32
+ *     tiles, so seqlen must then be a multiple of 32); head_dim in {64, 96, 128};
+ *     seqlen must be a positive multiple of block.  Block sizes 64 and 128 are
+ *     selected by wise_build_support_blocked on 32-token masses.
+ *     scale <= 0 selects 1/sqrt(head_dim).
  */
 #ifndef WISE_H_
 #define WISE_H_
@@ -66,11 +70,12 @@ const char* wise_status_string(wise_status s);
  *   q, k, v, o : [batch][heads][seqlen][head_dim] of dtype dt; o is written.
  *   lse        : NULL, or fp32 [batch*heads*seqlen] receiving the natural-log
  *                log-sum-exp of every query row's scaled logits.
- *   mass       : NULL, or fp32 [batch*heads][nq][nq] receiving the block mass of
- *                the WISE paper §5.1 (Eq. 5):
+ *   mass       : NULL, or fp32 [batch*heads][nq][nq] (nq = seqlen / block)
+ *                receiving the block mass of the WISE paper §5.1 (Eq. 5):
  *                  mass[bh][q][b] = (1/block) sum_{i in query block q}
  *                                   sum_{j in key block b, j <= i} A_ij,
  *                with A the attention probabilities above; entries b > q are 0.
+ *                At block 16 each 32 x 32 tile yields its four 16 x 16 sums.
  *                The masses are computed from fp32 probabilities in a second
  *                sweep over the keys once each row's log-sum-exp is known.
  * With mass == NULL this is the dense baseline kernel.
@@ -220,20 +225,25 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  * from the schedule are skipped, not masked.  Fresh q, k, v every call.
  *   q, k, v, o, lse, scale : as for wise_full_attn_mass (lse may be NULL).
  *   row_ptr, col_idx       : the schedule (as produced by wise_build_support),
- *                            rows ordered (b*heads + h)*nq + q.
+ *                            rows ordered (b*heads + h)*nq + q, nq = seqlen / block;
+ *                            at block 16 the rows and key blocks are 16-token
+ *                            blocks (wise_build_support on 16-token masses) and the
+ *                            kernels mask the unscheduled 16 x 16 sub-blocks of the
+ *                            32 x 32 tiles they visit.
  *   col_capacity           : number of readable col_idx entries.
  *   plan, plan_capacity    : NULL, or the execution plan wise_build_support wrote
  *                            for this same schedule, plan_capacity its readable
  *                            int32 entries (>= G + 1).  When given, the bf16
  *                            kernel walks the plan instead of the CSR rows (same
  *                            result up to the order of floating-point summation);
- *                            the fp32 kernel ignores it.
+ *                            the fp32 kernel and block 16 ignore it.
  * Entries outside 0..q, and offsets outside 0..col_capacity (0..plan_capacity),
  * are ignored.  In the CSR a block listed twice counts once; a plan must come
  * from wise_build_support, which lists each block of a group once.  A row left
  * with no admissible key writes o = 0 and lse = -inf (wise_build_support never
  * produces one).  The bf16 kernel supports up to 4096 key blocks per head
- * (seqlen <= 131072); beyond that it returns WISE_ERR_UNSUPPORTED.
+ * (seqlen <= 131072), 2048 at block 16 (seqlen <= 32768); beyond that it
+ * returns WISE_ERR_UNSUPPORTED.
  */
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
                              int head_dim, int block, const void* q, const void* k, const void* v, void* o,

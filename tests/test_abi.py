@@ -84,7 +84,9 @@ def test_attention_validation(lib):
         assert _attn(lib, **{name: MIS}) == INVALID, name
     assert _attn(lib, n=100) == INVALID                 # seqlen not a multiple of the block
     assert _attn(lib, blk=64) == UNSUPPORTED
-    assert _attn(lib, blk=16) == UNSUPPORTED
+    assert _attn(lib, blk=8) == UNSUPPORTED
+    assert _attn(lib, blk=16, n=48) == UNSUPPORTED      # 16-token blocks still tile 32 queries
+    assert _attn(lib, blk=16, n=40) == INVALID          # not a multiple of the block
     assert _attn(lib, d=80) == UNSUPPORTED
     for hk in (0, -1, 3, 4):                         # kv heads must divide heads (h = 2) and not exceed it
         assert _attn(lib, hk=hk) == INVALID, hk
@@ -157,6 +159,8 @@ def test_sparse_validation(lib):
     assert sp(n=96 + 1) == INVALID
     assert sp(d=256) == UNSUPPORTED
     assert sp(n=32 * 4097) == UNSUPPORTED              # bf16 rows beyond 4096 key blocks
+    assert sp(n=32 * 1025, blk=16) == UNSUPPORTED      # ... beyond 2048 16-token key blocks
+    assert sp(n=48, blk=16) == UNSUPPORTED
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
     assert sp(d=80) == UNSUPPORTED

@@ -115,3 +115,121 @@ def test_blocked_end_to_end(block):
         ro, rl = O.sparse_attention(f64(qs[0, h]), f64(ks[0, h]), f64(vs[0, h]), sup_b, block=block)
         assert_attn_close(f64(o[0, h])[same], ro[same], w.dtype, f"B={block} head {h} O")
         assert_lse_close(f64(lse[0, h])[same], rl[same], w.dtype, f"B={block} head {h}")
+
+
+# ----------------------------------------------------------------- 16-token blocks
+#
+# B = 16 (finer than the 32 x 32 tiles): the discovery kernel writes 16-token
+# masses (sums per 16 x 16 sub-block of its tiles), the plain builder selects on
+# them, and the sparse kernels take the 16-token CSR, masking the unscheduled
+# sub-blocks of the tiles they visit.  Pinned against the oracle's definitions at
+# block 16.
+
+def _b16_inputs(name, step, heads=None):
+    w, g = WORKLOADS[name], _gen(name)
+    q, k, v = g.step_torch(step)
+    hs = range(w.heads) if heads is None else heads
+    return w, q, k, v, hs
+
+
+@pytest.mark.parametrize("name", ["tiny", "1k", "d96", "gqa"])
+def test_block16_masses_match_oracle(name):
+    wise = _wise()
+    w, q, k, v, hs = _b16_inputs(name, 10)
+    note(f"b16 mass {name}")
+    o, lse, mass = wise.full_attn_mass(q.to(DEV), k.to(DEV), v.to(DEV), want_lse=True, want_mass=True, block=16)
+    torch.cuda.synchronize()
+    nq16 = w.seqlen // 16
+    assert tuple(mass.shape) == (w.heads, nq16, nq16)
+    mg = f64(mass)
+    for h in hs:
+        ref = O.block_mass(f64(q[0, h]), f64(k[0, h // w.group]), block=16)
+        err = np.abs(mg[h] - ref)
+        tol = 1e-6 if w.dtype == "fp32" else 2e-5
+        assert float(err.max()) <= tol, f"{name} head {h}: mass err {float(err.max()):.3e}"
+        assert np.all(mg[h][np.triu_indices(nq16, 1)] == 0.0)
+        ro, rl = O.causal_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]))
+        assert_attn_close(f64(o[0, h]), ro, w.dtype, f"{name} head {h} O (block 16)")
+        assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} head {h} lse (block 16)")
+
+
+def _random_rows16(rng, nq16, density):
+    """16-token supports with the awkward cases: diagonal-only rows, rows whose
+    first scheduled block sits in a later tile than the other query half's, empty
+    rows, and blocks above the row (which must be ignored)."""
+    rows = []
+    for q in range(nq16):
+        kind = rng.integers(6)
+        if kind == 0:
+            sup = [q]
+        elif kind == 1:
+            sup = []
+        elif kind == 2:
+            sup = sorted(set(rng.integers(0, q + 1, size=2).tolist()) | {q, min(q + 3, nq16 - 1)})
+        else:
+            sup = sorted(set(np.nonzero(rng.random(q + 1) < density)[0].tolist()) | {0})
+        rows.append(np.array(sup, dtype=np.int64))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["tiny", "1k", "gqa"])
+def test_block16_sparse_on_random_schedule(name):
+    wise = _wise()
+    w, q, k, v, hs = _b16_inputs(name, 14)
+    nq16 = w.seqlen // 16
+    rng = np.random.default_rng(16 + nq16)
+    sups = [_random_rows16(rng, nq16, 0.3) for _ in range(w.heads)]
+    from parity_helpers import schedule_from_rows
+    sched = schedule_from_rows([r for s in sups for r in s], DEV)
+    note(f"b16 sparse {name}")
+    o, lse = wise.sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), sched, want_lse=True, block=16)
+    torch.cuda.synchronize()
+    for h in hs:
+        valid = [r[r <= qq] for qq, r in enumerate(sups[h])]
+        ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]), valid, block=16)
+        assert_attn_close(f64(o[0, h]), ro, w.dtype, f"{name} head {h} O (block 16)")
+        assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} head {h} lse (block 16)")
+
+
+def test_block16_end_to_end():
+    """GPU 16-token masses over steps 9..12 -> plain builder -> sparse step 20,
+    against the oracle's masses, supports (usual flags) and attention at B = 16."""
+    wise, w = _wise(), WORKLOADS["1k"]
+    eta = w.etas[0]
+    g = _gen("1k")
+    nq16 = w.seqlen // 16
+    mass = torch.empty((4, w.heads, nq16, nq16), dtype=torch.float32, device=DEV)
+    for si, t in enumerate((9, 10, 11, 12)):
+        q, k, v = g.step_torch(t, DEV)
+        wise.full_attn_mass(q, k, v, mass=mass[si], block=16)
+    note("b16 e2e")
+    sched = wise.build_support(mass, eta, with_plan=False)
+    torch.cuda.synchronize()
+    rows = csr_rows(sched.row_ptr, sched.col_idx)
+    m16 = _masses("1k", 16)
+    (qs, ks, vs), dev = step_pair(g, 20)
+    o, lse = wise.sparse_attn(*dev, sched, want_lse=True, block=16)
+    torch.cuda.synchronize()
+    n32 = 0
+    for h in range(w.heads):
+        sup, same = [], np.zeros(w.seqlen, dtype=bool)
+        for qb in range(nq16):
+            s_, fl = O.union_supports([[O.select_support(m16[s, h, qb, :qb + 1], eta)] for s in range(4)])[0], set()
+            for s in range(4):
+                fc, ft = O.boundary_flags(m16[s, h, qb, :qb + 1], eta)
+                fl |= set(int(b) for b in np.nonzero(fc | ft)[0])
+            sup.append(s_)
+            diff = set(rows[h * nq16 + qb].tolist()) ^ set(s_.tolist())
+            assert diff <= fl, f"B=16 head {h} row {qb}: {diff}"
+            if not diff:
+                same[16 * qb:16 * qb + 16] = True
+            n32 += len(s_)
+        ro, rl = O.sparse_attention(f64(qs[0, h]), f64(ks[0, h]), f64(vs[0, h]), sup, block=16)
+        assert_attn_close(f64(o[0, h])[same], ro[same], w.dtype, f"B=16 head {h} O")
+        assert_lse_close(f64(lse[0, h])[same], rl[same], w.dtype, f"B=16 head {h}")
+    # the 16-token working set keeps fewer keys than the 32-token one (Table 8's
+    # ordering of densities, on this workload)
+    s32 = wise.build_support(torch.from_numpy(_masses("1k", 32).astype(np.float32)).to(DEV), eta, with_plan=False)
+    keys16 = 16 * 16 * n32
+    keys32 = 32 * 32 * int(s32.nnz.item())
+    assert keys16 < keys32
