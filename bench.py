@@ -397,7 +397,7 @@ def main():
         "timed_wall_s": round(wall, 3),
         "support_diagnostics": diagnostics,
         "roofline": {
-            "kernel": "wise_sparse_attn: attn_sparse_kernel<128>",
+            "kernel": "wise_sparse_attn: attn_sparse_kernel<128, 2>",
             "bound": "mfma",
             "achieved": round(tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
