@@ -352,8 +352,17 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // longer (fewer barriers, more loads in flight)
   constexpr int TRIP = SPARSE ? kSparseTrip : 2;
 
-  __shared__ __attribute__((aligned(16))) __bf16 kt[TRIP][32 * T::KSTRIDE];
-  __shared__ __attribute__((aligned(16))) __bf16 vt[TRIP][32 * T::VSTRIDE];
+  // the trip's K and V tiles; the block-mass sweep reuses the same LDS for
+  // MTRIP K-only tiles per trip
+  constexpr int MTRIP = 4;
+  typedef __bf16 KTile[32 * T::KSTRIDE];
+  typedef __bf16 VTile[32 * T::VSTRIDE];
+  constexpr size_t TILES_BYTES = TRIP * (sizeof(KTile) + sizeof(VTile));
+  constexpr size_t SWEEP_BYTES = MASS ? MTRIP * sizeof(KTile) : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_tiles[TILES_BYTES > SWEEP_BYTES ? TILES_BYTES : SWEEP_BYTES];
+  KTile* const kt = reinterpret_cast<KTile*>(lds_tiles);
+  VTile* const vt = reinterpret_cast<VTile*>(lds_tiles + TRIP * sizeof(KTile));
+  KTile* const mk = reinterpret_cast<KTile*>(lds_tiles);
   __shared__ uint32_t rmask[SPARSE ? W * kMaxMaskWords : 1];
   __shared__ uint32_t smask[SUB ? W * 2 * kSubWords : 1];  // the two 16-token rows of each wavefront
 
@@ -567,41 +576,115 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     constexpr bool B16 = MODE == kDenseMass16;
     const int nm = B16 ? 2 * a.nq : a.nq;  // mass row length
     float* mrow = a.mass + (size_t)(bh * a.nq + qb) * (B16 ? 4 * a.nq : a.nq);
-    DenseList mlist{0, qlast + 1};
-    stream(mlist, false, [&](const int (&c)[TRIP]) {
+    // K tiles 0..qlast, MTRIP per trip, through mk[] (same trip discipline as
+    // stream(): loads one trip ahead in registers, each waited for in its trip)
+    auto sweep = [&](auto&& work) {
+      bf16x8 rk[MTRIP][CPT];
+      auto gk = [&](bf16x8 (&r)[CPT], int b) {
 #pragma unroll
-      for (int buf = 0; buf < TRIP; ++buf) {
-        const int b = c[buf] >> kEntryShift;
-        if (c[buf] < 0 || !active || b > qb) continue;
-        bf16x8 kf[T::NC];
-        load_frag<D>(kf, &kt[buf][i * T::KSTRIDE], h);
-        floatx16 s = qk_tile<D>(kf, qf);
-        float part[2] = {0.f, 0.f};
+        for (int u = 0; u < CPT; ++u) {
+          const int c = tid + NTHR * u;
+          if (CHUNKS % NTHR == 0 || c < CHUNKS)
+            r[u] = *reinterpret_cast<const bf16x8*>(kh + (size_t)(32 * b + c / T::C8) * D + (c % T::C8) * 8);
+        }
+      };
+      auto sk = [&](const bf16x8 (&r)[CPT], int buf) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+          const int c = tid + NTHR * u;
+          if (CHUNKS % NTHR == 0 || c < CHUNKS)
+            *reinterpret_cast<bf16x8*>(&mk[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = r[u];
+        }
+      };
+      int c[MTRIP];
+#pragma unroll
+      for (int u = 0; u < MTRIP; ++u) c[u] = u <= qlast ? u : -1;
+#pragma unroll
+      for (int u = 0; u < MTRIP; ++u)
+        if (c[u] >= 0) gk(rk[u], c[u]);
+#pragma unroll
+      for (int u = 0; u < MTRIP; ++u)
+        if (c[u] >= 0) sk(rk[u], u);
+      __syncthreads();
+      while (c[0] >= 0) {
+        int n[MTRIP];
+#pragma unroll
+        for (int u = 0; u < MTRIP; ++u) n[u] = c[0] + MTRIP + u <= qlast ? c[0] + MTRIP + u : -1;
+#pragma unroll
+        for (int u = 0; u < MTRIP; ++u)
+          if (n[u] >= 0) gk(rk[u], n[u]);
+        work(c);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < MTRIP; ++u)
+          if (n[u] >= 0) sk(rk[u], u);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < MTRIP; ++u) c[u] = n[u];
+      }
+    };
+    sweep([&](const int (&c)[MTRIP]) {
+      if (!active) return;
+      // all of the trip's tiles at once: independent MFMA chains, then the
+      // exponentials and one interleaved lane reduction per 16 x 16 (B = 16) or
+      // 32 x 32 (B = 32) block; a tile past the end (c < 0) or above the row is
+      // computed on whatever the buffer holds and not written
+      floatx16 sv[MTRIP];
+#pragma unroll
+      for (int buf = 0; buf < MTRIP; ++buf) sv[buf] = floatx16{};
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int cc = 0; cc < T::NC; ++cc)
+#pragma unroll
+        for (int buf = 0; buf < MTRIP; ++buf) {
+          const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&mk[buf][i * T::KSTRIDE + h * T::HALF + 8 * cc]);
+          sv[buf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf.get(cc), sv[buf], 0, 0, 0);
+        }
+      __builtin_amdgcn_s_setprio(0);
+      float x[MTRIP][2];
+#pragma unroll
+      for (int buf = 0; buf < MTRIP; ++buf) {
+        const int b = c[buf];
+        x[buf][0] = x[buf][1] = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(s[r], a.scale_log2, -lse2));
+          float p = fast_exp2(fmaf(sv[buf][r], a.scale_log2, -lse2));
           if (b == qb && acc_row(r, h) > i) p = 0.f;
-          part[r >> 3] += p;
+          x[buf][r >> 3] += p;
         }
-        if (!B16) {
-          const float tot = wave_sum(part[0] + part[1]);
-          if (lane == 0) mrow[b] = tot * (1.f / 32.f);
-        } else {
+        if (!B16) x[buf][0] += x[buf][1];
+      }
+      // 16-lane row sums land in lanes 15, 31, 47, 63 (rows 0 and 2 hold query
+      // block 2 qb's lanes at B = 16, rows 1 and 3 query block 2 qb + 1's)
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            float x = part[kh];  // 16-lane row sums land in lanes 15, 31, 47, 63
-            x += row_shr<1>(x);
-            x += row_shr<2>(x);
-            x += row_shr<4>(x);
-            x += row_shr<8>(x);
-            const int xi = __float_as_int(x);
-            const float s0 = __int_as_float(__builtin_amdgcn_readlane(xi, 15)) +
-                             __int_as_float(__builtin_amdgcn_readlane(xi, 47));
-            const float s1 = __int_as_float(__builtin_amdgcn_readlane(xi, 31)) +
-                             __int_as_float(__builtin_amdgcn_readlane(xi, 63));
-            if (lane == 0) {
-              mrow[2 * b + kh] = s0 * (1.f / 16.f);       // query block 2 qb
-              mrow[nm + 2 * b + kh] = s1 * (1.f / 16.f);  // query block 2 qb + 1
+      for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+        for (int buf = 0; buf < MTRIP; ++buf)
+#pragma unroll
+          for (int kh = 0; kh < (B16 ? 2 : 1); ++kh) {
+            const float y = d == 1   ? row_shr<1>(x[buf][kh])
+                            : d == 2 ? row_shr<2>(x[buf][kh])
+                            : d == 4 ? row_shr<4>(x[buf][kh])
+                                     : row_shr<8>(x[buf][kh]);
+            x[buf][kh] += y;
+          }
+#pragma unroll
+      for (int buf = 0; buf < MTRIP; ++buf) {
+        const int b = c[buf];
+        if (c[buf] < 0 || b > qb) continue;
+#pragma unroll
+        for (int kh = 0; kh < (B16 ? 2 : 1); ++kh) {
+          const int xi = __float_as_int(x[buf][kh]);
+          const float r0 = __int_as_float(__builtin_amdgcn_readlane(xi, 15));
+          const float r1 = __int_as_float(__builtin_amdgcn_readlane(xi, 31));
+          const float r2 = __int_as_float(__builtin_amdgcn_readlane(xi, 47));
+          const float r3 = __int_as_float(__builtin_amdgcn_readlane(xi, 63));
+          if (lane == 0) {
+            if (!B16) {
+              mrow[b] = ((r0 + r1) + (r2 + r3)) * (1.f / 32.f);
+            } else {
+              mrow[2 * b + kh] = (r0 + r2) * (1.f / 16.f);       // query block 2 qb
+              mrow[nm + 2 * b + kh] = (r1 + r3) * (1.f / 16.f);  // query block 2 qb + 1
             }
           }
         }
