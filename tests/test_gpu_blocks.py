@@ -233,3 +233,38 @@ def test_block16_end_to_end():
     keys16 = 16 * 16 * n32
     keys32 = 32 * 32 * int(s32.nnz.item())
     assert keys16 < keys32
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d,heads,kv,n", [(64, 4, 2, 256), (96, 2, 1, 320), (128, 3, 3, 192)])
+def test_block16_shapes_batch_gqa(dtype, d, heads, kv, n):
+    """16-token masses and sparse steps with batch 2, grouped-query heads, every
+    head_dim and a sequence that is not a multiple of 128."""
+    wise = _wise()
+    rng = np.random.default_rng(d * 7 + n)
+    b = 2
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.from_numpy(rng.standard_normal((b, heads, n, d)).astype(np.float32) * 1.3).to(tdt)
+    k = torch.from_numpy(rng.standard_normal((b, kv, n, d)).astype(np.float32) * 1.3).to(tdt)
+    v = torch.from_numpy(rng.standard_normal((b, kv, n, d)).astype(np.float32)).to(tdt)
+    nq16, grp = n // 16, heads // kv
+    note(f"b16 shapes {dtype} d={d} h={heads}/{kv} n={n}")
+    o, lse, mass = wise.full_attn_mass(q.to(DEV), k.to(DEV), v.to(DEV), want_lse=True, want_mass=True, block=16)
+    sups = [_random_rows16(rng, nq16, 0.4) for _ in range(b * heads)]
+    from parity_helpers import schedule_from_rows
+    sched = schedule_from_rows([r for s in sups for r in s], DEV)
+    os_, ls_ = wise.sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), sched, want_lse=True, block=16)
+    torch.cuda.synchronize()
+    mg = f64(mass)
+    tol = 1e-6 if dtype == "fp32" else 2e-5
+    for bi in range(b):
+        for h in range(heads):
+            qh, kh, vh = f64(q[bi, h]), f64(k[bi, h // grp]), f64(v[bi, h // grp])
+            ref = O.block_mass(qh, kh, block=16)
+            assert float(np.abs(mg[bi * heads + h] - ref).max()) <= tol, f"mass b={bi} h={h}"
+            ro, rl = O.causal_attention(qh, kh, vh)
+            assert_attn_close(f64(o[bi, h]), ro, dtype, f"dense O b={bi} h={h}")
+            valid = [r[r <= qq] for qq, r in enumerate(sups[bi * heads + h])]
+            so, sl = O.sparse_attention(qh, kh, vh, valid, block=16)
+            assert_attn_close(f64(os_[bi, h]), so, dtype, f"sparse O b={bi} h={h}")
+            assert_lse_close(f64(ls_[bi, h]), sl, dtype, f"sparse lse b={bi} h={h}")
