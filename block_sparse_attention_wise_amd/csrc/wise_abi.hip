@@ -225,7 +225,8 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
   if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
   if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
   if (dt == WISE_BF16 && seqlen / kBlock > kMaxSparseBlocks) return WISE_ERR_UNSUPPORTED;
-  if (dt == WISE_BF16 && block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
+  // 16-token rows are bitmasks of 2048 blocks in both kernels' LDS
+  if (block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
   if (plan != nullptr) {
     const int64_t groups = (int64_t)batch * heads * ((seqlen / kBlock + kPlanRows - 1) / kPlanRows);
     if (!aligned4(plan) || plan_capacity < groups + 1) return WISE_ERR_INVALID_ARG;

@@ -160,6 +160,7 @@ def test_sparse_validation(lib):
     assert sp(d=256) == UNSUPPORTED
     assert sp(n=32 * 4097) == UNSUPPORTED              # bf16 rows beyond 4096 key blocks
     assert sp(n=32 * 1025, blk=16) == UNSUPPORTED      # ... beyond 2048 16-token key blocks
+    assert sp(n=32 * 1025, blk=16, dt=FP32) == UNSUPPORTED  # (both kernels)
     assert sp(n=48, blk=16) == UNSUPPORTED
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
