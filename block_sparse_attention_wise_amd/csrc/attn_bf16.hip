@@ -139,10 +139,15 @@ __device__ __forceinline__ float max_tree3(const float (&v)[K]) {
 // 16 x 16 sub-blocks of tile n are scheduled (bit 2 qh + kh: query half qh, key
 // half kh); keys of unscheduled sub-blocks are masked like non-causal ones, and
 // a query half with no key yet keeps l = 0 and O = 0.
-template <int D, int N, class QS, bool SUB = false>
+// BL = 32 or 16 (the block-mass modes): with blse set, each tile's per-query
+// log-sum-exps of its scaled logits over keys 0..15 and 16..31 (log2 units) are
+// stored at blse + bidx[n] * 64 + {0, 32} + query, where the block-mass epilogue
+// reads them back.
+template <int D, int N, class QS, bool SUB = false, int BL = 0>
 __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* const (&kt)[N], const QS& qf,
                                              const __bf16* const (&vt)[N], const bool (&diag)[N], int i, int h,
-                                             int lane, float sl2, int sub_bits = 0xFF) {
+                                             int lane, float sl2, int sub_bits = 0xFF, float* blse = nullptr,
+                                             const int* bidx = nullptr) {
   using T = Tile<D>;
   floatx16 s[N];
 #pragma unroll
@@ -210,11 +215,23 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
       p[r] = fast_exp2(fmaf(s[n][r], sl2, -m_use));
       pb[r >> 3][r & 7] = (__bf16)p[r];
     }
+    if constexpr (BL != 0) {
+      // registers 0..7 hold keys 0..15 of the tile, 8..15 keys 16..31
+      float x0 = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      float x1 = ((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15]));
+      lsum += x0 + x1;
+      if (blse != nullptr) {
+        x0 = halves_sum(x0);
+        x1 = halves_sum(x1);
+        blse[bidx[n] * kMassWsSlot + 32 * h + i] = __builtin_amdgcn_logf(h ? x1 : x0) + m_use;
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) p[r] += p[r + 8];
+      for (int r = 0; r < 8; ++r) p[r] += p[r + 8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] += p[r + 4];
-    lsum += (p[0] + p[2]) + (p[1] + p[3]);
+      for (int r = 0; r < 4; ++r) p[r] += p[r + 4];
+      lsum += (p[0] + p[2]) + (p[1] + p[3]);
+    }
 #pragma unroll
     for (int t = 0; t < T::NT; ++t)
 #pragma unroll
@@ -343,6 +360,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   constexpr bool SPARSE = MODE == kSparse || MODE == kSparse16;
   constexpr bool SUB = MODE == kSparse16;
   constexpr bool MASS = MODE == kDenseMass || MODE == kDenseMass16;
+  constexpr int BL = MODE == kDenseMass ? 32 : MODE == kDenseMass16 ? 16 : 0;  // one-pass block-mass store
   constexpr int W = SPARSE ? kSparseWaves : kWaves;  // wavefronts = query blocks per workgroup
   constexpr int NTHR = 64 * W;
   constexpr int CHUNKS = 32 * T::C8;                // 16-byte chunks of one tile
@@ -506,6 +524,12 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
 
   RowState<D> st;
   st.init();
+  // one-pass block mass: this query block's per-tile log-sum-exp slots, a
+  // triangle of key tiles 0..qb per (batch, head) row
+  float* const blse = MASS && a.mass_ws != nullptr && active
+                          ? a.mass_ws + ((size_t)bh * ((size_t)a.nq * (a.nq + 1) / 2) + (size_t)qb * (qb + 1) / 2) *
+                                            kMassWsSlot
+                          : nullptr;
   // a trip's tiles of this wavefront's row, two per softmax step
   // 16-token blocks: which 16 x 16 sub-blocks of tile b this wavefront's two rows
   // schedule (bit 2 x + kh: row 2 qb + x, key block 2 b + kh)
@@ -531,8 +555,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const __bf16* const kp[2] = {kt[u0], kt[u1]};
       const __bf16* const vp[2] = {vt[u0], vt[u1]};
       const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
-      attend_tiles<D, 2, QRegs<D>, SUB>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
-                                        sub4(c[u0] >> kEntryShift) | (sub4(c[u1] >> kEntryShift) << 4));
+      const int bi[2] = {c[u0] >> kEntryShift, c[u1] >> kEntryShift};
+      attend_tiles<D, 2, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
+                                            sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi);
     }
     while (mine) {
       const int u0 = __builtin_ctz(mine);
@@ -540,8 +565,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const __bf16* const kp[1] = {kt[u0]};
       const __bf16* const vp[1] = {vt[u0]};
       const bool dp[1] = {((dg >> u0) & 1) != 0};
-      attend_tiles<D, 1, QRegs<D>, SUB>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
-                                        sub4(c[u0] >> kEntryShift) | 0xF0);
+      const int bi[1] = {c[u0] >> kEntryShift};
+      attend_tiles<D, 1, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2, sub4(bi[0]) | 0xF0,
+                                            blse, bi);
     }
   };
   if (SPARSE && !SUB && a.plan != nullptr) {
@@ -568,7 +594,51 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     lse2 = finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
   }
 
-  if (MASS) {
+  if (MASS && a.mass_ws != nullptr) {
+    // Block mass (Eq. 5) from the stored block log-sum-exps: with L_ib the
+    // log-sum-exp of query i's scaled logits over the keys of block b (j <= i)
+    // and lse_i the row's, r_qb = (1/B) sum_{i in q} exp(L_ib - lse_i) (log2
+    // units here).  Lane l takes key tile b = l (+ 64 per pass): it reads the
+    // tile's 32 (B = 32) or 64 (B = 16: per query, keys 0..15 then 16..31)
+    // stored values in one burst and sums over the queries itself.
+    constexpr bool B16 = MODE == kDenseMass16;
+    constexpr int SLOT = kMassWsSlot;
+    const int nm = B16 ? 2 * a.nq : a.nq;  // mass row length
+    if (active) {
+      float* mrow = a.mass + (size_t)(bh * a.nq + qb) * (B16 ? 4 * a.nq : a.nq);
+      float lq[32];  // the 32 queries' log-sum-exps, wavefront-uniform
+#pragma unroll
+      for (int j = 0; j < 32; ++j) lq[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse2), j));
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wavefront's block log-sum-exp stores
+      for (int b = lane; b <= qb; b += 64) {
+        const floatx4* src = reinterpret_cast<const floatx4*>(blse + (size_t)b * SLOT);
+        floatx4 v[SLOT / 4];
+#pragma unroll
+        for (int c = 0; c < SLOT / 4; ++c) v[c] = src[c];
+        // sums over query halves qh (queries 16 qh .. 16 qh + 15) and key halves kh
+        float sum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+        for (int c = 0; c < SLOT / 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int qi = (4 * c + e) & 31, kh = (4 * c + e) >> 5;
+            sum[qi >> 4][kh] += fast_exp2(v[c][e] - lq[qi]);
+          }
+        if (!B16) {
+          mrow[b] = ((sum[0][0] + sum[1][0]) + (sum[0][1] + sum[1][1])) * (1.f / 32.f);
+        } else {
+          mrow[2 * b] = sum[0][0] * (1.f / 16.f);           // query block 2 qb, key block 2 b
+          mrow[2 * b + 1] = sum[0][1] * (1.f / 16.f);       // ... key block 2 b + 1
+          mrow[nm + 2 * b] = sum[1][0] * (1.f / 16.f);      // query block 2 qb + 1
+          mrow[nm + 2 * b + 1] = sum[1][1] * (1.f / 16.f);
+        }
+      }
+      for (int b = (B16 ? 2 : 1) * (qb + 1) + lane; b < nm; b += 64) {
+        mrow[b] = 0.f;
+        if (B16) mrow[nm + b] = 0.f;
+      }
+    }
+  } else if (MASS) {
     // Block mass (Eq. 5): r_qb = (1/B) sum_i sum_{j in b, j <= i} exp(s_ij - lse_i),
     // a second sweep over the keys now that every row's log-sum-exp is final.
     // B = 32: one value per tile; B = 16: one per 16 x 16 sub-block (registers

@@ -19,6 +19,7 @@ struct AttnBf16Args {
   __bf16* o;
   float* lse;                // nullable
   float* mass;               // nullable; dense kernel only
+  float* mass_ws;            // nullable: block log-sum-exp store of the one-pass mass epilogue
   const int32_t* row_ptr;    // sparse kernel only
   const int32_t* col_idx;    // sparse kernel only
   int64_t col_cap;           // readable col_idx entries (<= INT32_MAX)
@@ -57,6 +58,11 @@ hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bo
 hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, bool b16,
                            hipStream_t stream);
 size_t support_workspace_bytes(int bh, int nq);
+// floats of the one-pass block-mass store per (query block, key tile) pair (one
+// per query and 16-key half, at either block size), and its total size for bh
+// rows of nq tiles
+constexpr int kMassWsSlot = 64;
+size_t mass_ws_bytes(int64_t bh, int nq);
 size_t plan_capacity(int bh, int nq);
 // kind: 0 cumulative-eta support per step, unioned over the steps; 1 SizeMatched and
 // 2 MassMatched against the reference schedule (steps == 1)

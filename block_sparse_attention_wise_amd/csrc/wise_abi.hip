@@ -41,7 +41,7 @@ float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.
 
 wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
                      const void* q, const void* k, const void* v, void* o, float* lse, float* mass,
-                     const int32_t* row_ptr, const int32_t* col_idx, int64_t col_cap, const int32_t* plan,
+                     float* mass_ws, const int32_t* row_ptr, const int32_t* col_idx, int64_t col_cap, const int32_t* plan,
                      int64_t plan_cap, bool sparse, float scale, void* stream) {
   const bool b16 = block == kBlock / 2;
   if (col_cap > INT32_MAX) col_cap = INT32_MAX;
@@ -52,7 +52,7 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seql
   hipError_t e;
   if (dt == WISE_BF16) {
     AttnBf16Args a{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                   static_cast<__bf16*>(o), lse, mass, row_ptr, col_idx, col_cap, plan, plan_cap, seqlen, nq, rows,
+                   static_cast<__bf16*>(o), lse, mass, mass_ws, row_ptr, col_idx, col_cap, plan, plan_cap, seqlen, nq, rows,
                    heads, heads / kv_heads, sc * 1.4426950408889634f};
     e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, b16, static_cast<hipStream_t>(stream));
   } else {
@@ -85,6 +85,11 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
 }
 
 }  // namespace
+
+size_t mass_ws_bytes(int64_t bh, int nq) {
+  return (size_t)bh * ((size_t)nq * (nq + 1) / 2) * kMassWsSlot * sizeof(float);
+}
+
 }  // namespace wise
 
 using namespace wise;
@@ -103,21 +108,36 @@ const char* wise_status_string(wise_status s) {
   return "unknown status";
 }
 
+size_t wise_full_attn_mass_workspace_bytes(int batch, int heads, int seqlen, int block) {
+  if (batch <= 0 || heads <= 0 || seqlen <= 0 || seqlen % kBlock != 0) return 0;
+  if (block != kBlock && block != kBlock / 2) return 0;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh * (seqlen / block) > INT32_MAX) return 0;
+  return mass_ws_bytes(bh, seqlen / kBlock);
+}
+
 wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim,
                                 int block, const void* q, const void* k, const void* v, void* o, float* lse,
-                                float* mass, float scale, void* stream) {
+                                float* mass, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   wise_status st = check_attn_shape(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, scale);
   if (st != WISE_OK) return st;
   if (mass && !aligned4(mass)) return WISE_ERR_INVALID_ARG;
-  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, mass, nullptr, nullptr, 0,
-                  nullptr, 0, false, scale, stream);
+  float* ws = nullptr;
+  if (mass && workspace && dt == WISE_BF16) {
+    if (!aligned16(workspace) ||
+        workspace_bytes < wise_full_attn_mass_workspace_bytes(batch, heads, seqlen, block))
+      return WISE_ERR_INVALID_ARG;
+    ws = static_cast<float*>(workspace);
+  }
+  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, mass, ws, nullptr, nullptr,
+                  0, nullptr, 0, false, scale, stream);
 }
 
 wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
                             const void* q, const void* k, const void* v, void* o, float* lse, float scale,
                             void* stream) {
   return wise_full_attn_mass(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, scale,
-                             stream);
+                             nullptr, 0, stream);
 }
 
 size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps) {
@@ -233,7 +253,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
     // the fp32 kernel and 16-token schedules walk the CSR rows
     if (dt != WISE_BF16 || block != kBlock) plan = nullptr;
   }
-  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, row_ptr, col_idx,
+  return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, nullptr, row_ptr, col_idx,
                   col_capacity, plan, plan_capacity, true, scale, stream);
 }
 

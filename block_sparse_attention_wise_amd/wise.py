@@ -19,9 +19,10 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 EXPORTED = (
-    "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_dense_attn",
+    "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes",
+    "wise_dense_attn",
     "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity", "wise_build_support",
     "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
     "wise_build_support_blocked_workspace_bytes", "wise_build_support_blocked",
@@ -39,7 +40,10 @@ def _load():
     lib.wise_status_string.restype = ctypes.c_char_p
     lib.wise_status_string.argtypes = [i32]
     lib.wise_full_attn_mass.restype = i32
-    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp,
+                                        ctypes.c_size_t, vp]
+    lib.wise_full_attn_mass_workspace_bytes.restype = ctypes.c_size_t
+    lib.wise_full_attn_mass_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wise_dense_attn.restype = i32
     lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
     lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
@@ -131,11 +135,33 @@ def _f32_buf(t, numel, device, name):
     return t
 
 
+def full_attn_mass_workspace_bytes(b: int, h: int, n: int, block: int = BLOCK) -> int:
+    return int(lib.wise_full_attn_mass_workspace_bytes(b, h, n, block))
+
+
+_mass_ws_cache = {}
+
+
+def _mass_workspace(b, h, n, block, device):
+    """A cached device workspace for the one-pass block-mass epilogue."""
+    nbytes = full_attn_mass_workspace_bytes(b, h, n, block)
+    key = (str(device), nbytes)
+    ws = _mass_ws_cache.get(key)
+    if ws is None:
+        _mass_ws_cache.clear()
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _mass_ws_cache[key] = ws
+    return ws
+
+
 def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, want_mass=False,
-                   scale=None, block=BLOCK, stream=None):
+                   scale=None, block=BLOCK, workspace=None, stream=None):
     """Causal attention O (and optionally row LSE and block masses [b*h, nq, nq],
     nq = seqlen / block; block 32, or 16 for 16-token masses).
 
+    workspace: None (bf16 masses use a cached workspace and the one-pass epilogue),
+    False (no workspace: the second-sweep epilogue), or a caller's uint8 device tensor
+    of at least full_attn_mass_workspace_bytes(...) bytes.
     Returns (out, lse, mass); lse / mass are None unless passed or requested.
     """
     b, h, hk, n, d = _qkv_shape(q, k, v)
@@ -147,8 +173,15 @@ def full_attn_mass(q, k, v, *, out=None, lse=None, mass=None, want_lse=False, wa
         mass = torch.empty((b * h, nq, nq), dtype=torch.float32, device=q.device)
     lse = _f32_buf(lse, b * h * n, q.device, "lse")
     mass = _f32_buf(mass, b * h * nq * nq, q.device, "mass")
+    ws_ptr, ws_bytes = None, 0
+    if mass is not None and workspace is not False and q.dtype == torch.bfloat16:
+        if workspace is None:
+            workspace = _mass_workspace(b, h, n, block, q.device)
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     st = lib.wise_full_attn_mass(_dtype_code(q), b, h, hk, n, d, block, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                 _ptr(lse), _ptr(mass), float(scale or 0.0), _stream(stream))
+                                 _ptr(lse), _ptr(mass), float(scale or 0.0), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "wise_full_attn_mass")
     return out, lse, mass
 

@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 5
+#define WISE_ABI_VERSION 6
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -76,15 +76,35 @@ const char* wise_status_string(wise_status s);
  *                                   sum_{j in key block b, j <= i} A_ij,
  *                with A the attention probabilities above; entries b > q are 0.
  *                At block 16 each 32 x 32 tile yields its four 16 x 16 sums.
- *                The masses are computed from fp32 probabilities in a second
- *                sweep over the keys once each row's log-sum-exp is known.
+ *                The masses are computed from the fp32 probabilities of the
+ *                attention pass.
+ *   workspace  : NULL, or (bf16 with mass != NULL) device scratch of at least
+ *                wise_full_attn_mass_workspace_bytes(batch, heads, seqlen, block)
+ *                bytes, 16-byte aligned, owned by the caller; its contents on
+ *                entry do not matter.  With it, the attention pass stores every
+ *                (query, key block) log-sum-exp of the scaled logits there and
+ *                the masses follow from them and the final row log-sum-exp:
+ *                mass[bh][q][b] = (1/block) sum_i exp(L_ib - lse_i), Eq. 5
+ *                regrouped.  Without it (and always for fp32) a second sweep over
+ *                the keys recomputes the logits once the row log-sum-exp is
+ *                known.  Ignored when mass == NULL.  A workspace that is too
+ *                small or misaligned is WISE_ERR_INVALID_ARG.
  * With mass == NULL this is the dense baseline kernel.
  */
 wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
                                 int head_dim, int block, const void* q, const void* k, const void* v,
-                                void* o, float* lse, float* mass, float scale, void* stream);
+                                void* o, float* lse, float* mass, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
-/* Dense causal attention: wise_full_attn_mass with mass = NULL. */
+/*
+ * Bytes of the optional wise_full_attn_mass workspace (0 on invalid sizes):
+ * 4 * batch*heads * T * 64 with T = nt (nt + 1) / 2 (nt = seqlen / 32: the causal
+ * triangle of 32 x 32 tiles) and 64 floats per tile (one per query and 16-key
+ * half), at block 32 and 16 alike.
+ */
+size_t wise_full_attn_mass_workspace_bytes(int batch, int heads, int seqlen, int block);
+
+/* Dense causal attention: wise_full_attn_mass with mass = NULL and no workspace. */
 wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
                             int head_dim, int block, const void* q, const void* k, const void* v,
                             void* o, float* lse, float scale, void* stream);

@@ -31,7 +31,10 @@ def lib():
         pytest.fail("libwise.so is not built (run python -m block_sparse_attention_wise_amd.build)")
     lib = ctypes.CDLL(LIB)
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
-    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp]
+    lib.wise_full_attn_mass.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32, vp,
+                                        ctypes.c_size_t, vp]
+    lib.wise_full_attn_mass_workspace_bytes.restype = ctypes.c_size_t
+    lib.wise_full_attn_mass_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wise_dense_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
     lib.wise_build_support_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
@@ -54,7 +57,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) >= {"wise_full_attn_mass", "wise_dense_attn", "wise_build_support",
+    assert set(names) >= {"wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes", "wise_dense_attn",
+                          "wise_build_support",
                           "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity",
                           "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
                           "wise_build_support_blocked", "wise_build_support_blocked_workspace_bytes",
@@ -64,15 +68,36 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 5
+    assert lib.wise_abi_version() == 6
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
 
 
 def _attn(lib, dt=BF16, b=1, h=2, hk=None, n=128, d=128, blk=32, q=P, k=P, v=P, o=P2, lse=None, mass=None,
-          scale=0.0):
-    return lib.wise_full_attn_mass(dt, b, h, h if hk is None else hk, n, d, blk, q, k, v, o, lse, mass, scale, None)
+          scale=0.0, ws=None, wsb=0):
+    return lib.wise_full_attn_mass(dt, b, h, h if hk is None else hk, n, d, blk, q, k, v, o, lse, mass, scale, ws,
+                                   wsb, None)
+
+
+def test_mass_workspace_bytes(lib):
+    f = lib.wise_full_attn_mass_workspace_bytes
+    assert f(0, 1, 64, 32) == 0 and f(1, 0, 64, 32) == 0 and f(1, 1, 0, 32) == 0
+    assert f(1, 1, 48, 32) == 0 and f(1, 1, 64, 64) == 0 and f(1, 1, 64, 8) == 0
+    # the causal triangle of 32 x 32 tiles, 64 floats per tile (per query and 16-key half)
+    for b, h, n in ((1, 1, 32), (2, 3, 128), (1, 32, 4096)):
+        nt = n // 32
+        assert f(b, h, n, 32) == 4 * b * h * nt * (nt + 1) // 2 * 64
+        assert f(b, h, n, 16) == f(b, h, n, 32)
+
+
+def test_mass_workspace_validation(lib):
+    need = lib.wise_full_attn_mass_workspace_bytes(1, 2, 128, 32)
+    m = ctypes.c_void_p(0x20000)
+    assert _attn(lib, mass=m, ws=ctypes.c_void_p(0x30008), wsb=need) == INVALID     # misaligned
+    assert _attn(lib, mass=m, ws=P2, wsb=need - 4) == INVALID                     # too small
+    need16 = lib.wise_full_attn_mass_workspace_bytes(1, 2, 128, 16)
+    assert _attn(lib, mass=m, blk=16, ws=P2, wsb=need16 - 4) == INVALID
 
 
 def test_attention_validation(lib):

@@ -132,12 +132,14 @@ def _b16_inputs(name, step, heads=None):
     return w, q, k, v, hs
 
 
+@pytest.mark.parametrize("epilogue", ["one-pass", "sweep"])
 @pytest.mark.parametrize("name", ["tiny", "1k", "d96", "gqa"])
-def test_block16_masses_match_oracle(name):
+def test_block16_masses_match_oracle(name, epilogue):
     wise = _wise()
     w, q, k, v, hs = _b16_inputs(name, 10)
-    note(f"b16 mass {name}")
-    o, lse, mass = wise.full_attn_mass(q.to(DEV), k.to(DEV), v.to(DEV), want_lse=True, want_mass=True, block=16)
+    note(f"b16 mass {name} {epilogue}")
+    o, lse, mass = wise.full_attn_mass(q.to(DEV), k.to(DEV), v.to(DEV), want_lse=True, want_mass=True, block=16,
+                                       workspace=None if epilogue == "one-pass" else False)
     torch.cuda.synchronize()
     nq16 = w.seqlen // 16
     assert tuple(mass.shape) == (w.heads, nq16, nq16)

@@ -101,3 +101,25 @@ def test_fullsize_dense_rows(name):
             sl = slice(32 * qb, 32 * qb + 32)
             assert_attn_close(f64(o[0, h, sl]), ro, w.dtype, f"{name} head {h} block {qb} O")
             assert_lse_close(f64(lse[0, h, sl]), rl, w.dtype, f"{name} head {h} block {qb}")
+
+
+@pytest.mark.parametrize("name,block", [("4k", 32), ("4k", 16), ("huginn4k", 32)])
+def test_fullsize_mass_epilogues_agree(name, block):
+    """At the full size, the one-pass block masses (from stored block log-sum-exps)
+    equal the second-sweep masses (logits recomputed once the row log-sum-exp is
+    known) to fp32 rounding, over every (head, query block, key block)."""
+    from block_sparse_attention_wise_amd import wise
+    w = WORKLOADS[name]
+    _, dq = step_pair(Generator(w), 10)
+    note(f"{name} block {block} mass epilogues")
+    _, _, m1 = wise.full_attn_mass(*dq, want_mass=True, block=block)
+    _, _, m2 = wise.full_attn_mass(*dq, want_mass=True, block=block, workspace=False)
+    torch.cuda.synchronize()
+    d = (m1 - m2).abs()
+    assert float(d.max()) <= 2e-5, f"max |one-pass - sweep| = {float(d.max()):.3e}"
+    nb = m1.shape[-1]
+    upper = torch.triu(torch.ones(nb, nb, dtype=torch.bool, device=m1.device), 1)
+    assert bool((m1[:, upper] == 0).all())
+    # every causal row sums to 1 (Eq. 5 over all key blocks is the row's total probability / B per query)
+    rs = m1.sum(-1)
+    assert float((rs - 1.0).abs().max()) <= 1e-4

@@ -45,12 +45,16 @@ def test_dense_attention(name):
         assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} head {h}")
 
 
+@pytest.mark.parametrize("epilogue", ["one-pass", "sweep"])
 @pytest.mark.parametrize("name", SMALL)
-def test_discovery_attention_and_block_mass(name):
+def test_discovery_attention_and_block_mass(name, epilogue):
+    """Both block-mass epilogues (stored block log-sum-exps, or a second sweep
+    over the keys) against the oracle's Eq. 5."""
     wise, w = _wise(), WORKLOADS[name]
     (q, k, v), dev = step_pair(_gen(name), 9)
-    note(f"mass {name}")
-    o, lse, mass = wise.full_attn_mass(*dev, want_lse=True, want_mass=True)
+    note(f"mass {name} {epilogue}")
+    o, lse, mass = wise.full_attn_mass(*dev, want_lse=True, want_mass=True,
+                                       workspace=None if epilogue == "one-pass" else False)
     torch.cuda.synchronize()
     for h in range(w.heads):
         qh, kh, vh = f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group])
