@@ -330,14 +330,15 @@ struct UnionList {
 };
 // a precomputed execution plan (wise_build_support): entries in trip order,
 // read 64 at a time, one per lane; entries naming a block past the group's last
-// query block, or with no row, are skipped
+// query block, or with no row, are skipped.  The first chunk is loaded up to
+// the group's slot end (limit) before the entry count is known.
 struct PlanList {
   const int32_t* e;
   int base, end, qlast, lane;
   int cur;
   int idx;  // next entry within the current chunk
-  __device__ __forceinline__ void load_chunk() {
-    cur = base + lane < end ? e[base + lane] : -1;
+  __device__ __forceinline__ void load_chunk(int limit) {
+    cur = base + lane < limit ? e[base + lane] : -1;
     idx = 0;
   }
   __device__ __forceinline__ int next() {
@@ -345,7 +346,7 @@ struct PlanList {
       if (idx == 64) {
         base += 64;
         if (base >= end) return -1;
-        load_chunk();
+        load_chunk(end);
       }
       if (base + idx >= end) return -1;
       const int v = __builtin_amdgcn_readlane(cur, idx++);
@@ -415,6 +416,18 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // (keeping the in-loop waits on the prefetched K/V tiles only).
   QRegs<D> qf;
   load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * min(qb, a.nq - 1) + i) * D, h);
+  // sparse mode with an execution plan: group g's entry count plan[g] and its
+  // first entries (fixed slot of nq entries) load together with Q
+  PlanList plist{nullptr, 0, 0, qlast, lane, -1, 64};
+  if (SPARSE && !SUB && a.plan != nullptr) {
+    const int groups = bhn * ngroups, g = bh * ngroups + grp;
+    const int slot = g * a.nq;  // plan capacity (checked on the host) covers every slot
+    plist.e = a.plan + groups + 1;
+    plist.base = slot;
+    plist.load_chunk(slot + a.nq);
+    const int cnt = a.plan[g];
+    plist.end = slot + (cnt < 0 ? 0 : (cnt > a.nq ? a.nq : cnt));
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   if (SPARSE && (a.plan == nullptr || SUB)) {
@@ -571,14 +584,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     }
   };
   if (SPARSE && !SUB && a.plan != nullptr) {
-    const int groups = bhn * ngroups, g = bh * ngroups + grp;
-    const int64_t cap = a.plan_cap - groups - 1;  // readable entries after the offsets
-    int64_t p0 = a.plan[g], p1 = a.plan[g + 1];
-    p0 = p0 < 0 ? 0 : (p0 > cap ? cap : p0);
-    p1 = p1 < p0 ? p0 : (p1 > cap ? cap : p1);
-    PlanList list{a.plan + groups + 1, (int)p0, (int)p1, qlast, lane, -1, 64};
-    if (list.base < list.end) list.load_chunk();
-    stream(list, true, attend);
+    stream(plist, true, attend);
   } else if (SPARSE) {
     UnionList<W> list{rmask, (qlast >> 5) + 1, 0, 0u};
     list.u = list.word_union(0);

@@ -252,28 +252,13 @@ static_assert(kPlanRows >= 1 && kPlanRows <= 8, "plan rows fit the 8-bit members
 static_assert(kPlanTrip >= 1 && kPlanTrip <= 16, "plan trip");
 constexpr int kMasks = 1 << kPlanRows;
 
-// union popcount of each group -> counts[g]
-__global__ __launch_bounds__(64) void group_count_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
-                                                         int32_t* counts) {
-  const int g = blockIdx.x, lane = threadIdx.x;
-  const int bh = g / ngroups, q0 = kPlanRows * (g - bh * ngroups);
-  const int qlast = min(q0 + kPlanRows, nq) - 1;
-  const int words = (qlast >> 5) + 1;
-  int c = 0;
-  for (int w = lane; w < words; w += 64) {
-    uint32_t u = 0u;
-    for (int r = q0; r <= qlast; ++r) u |= masks[(size_t)(bh * nq + r) * nwords + w];
-    c += __popc(u);
-  }
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-  if (lane == 0) counts[g] = c;
-}
-
 // one wavefront per group: collect (block, mask) tiles in ascending block order,
 // bucket them by mask (stable), then fill the trips greedily, every lane
-// scoring a quarter of the masks for each pick.
+// scoring a quarter of the masks for each pick.  The group's entries go to its
+// fixed slot of nq entries and their number to counts[g], so a reader finds
+// both without a prefix sum (and can load them together); counts[groups] = nq.
 __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
-                                                        const int32_t* plan_off, int32_t* entries) {
+                                                        int32_t* counts, int32_t* entries) {
   __shared__ int32_t tiles[kMaxNq];
   __shared__ int32_t sorted_tiles[kMaxNq];
   __shared__ int32_t bcount[kMasks], bstart[kMasks];
@@ -314,7 +299,9 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
     }
   }
   __syncthreads();
-  int32_t* out = entries + plan_off[g];
+  int32_t* out = entries + (size_t)g * nq;  // the group's fixed slot of nq entries
+  if (lane == 0) counts[g] = n;
+  if (g == 0 && lane == 0) counts[gridDim.x] = nq;
   int load[kPlanRows];
   for (int k = 0; k < n;) {
 #pragma unroll
@@ -350,9 +337,8 @@ size_t plan_capacity(int bh, int nq) {
 size_t support_workspace_bytes(int bh, int nq) {
   const size_t rows = (size_t)bh * nq;
   const size_t nwords = (nq + 31) / 32;
-  const size_t groups = (size_t)bh * ((nq + kPlanRows - 1) / kPlanRows);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al(rows * nwords * 4) + al(rows * 4) + al(groups * 4);
+  return al(rows * nwords * 4) + al(rows * 4);
 }
 
 // retained[row] = sum of mass[row][b] over the row's distinct scheduled blocks
@@ -407,16 +393,10 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, masks, nwords, row_ptr, col_idx);
   e = hipGetLastError();
   if (e != hipSuccess || plan == nullptr) return e;
-  // execution plan: plan[0..groups] = entry offsets, entries follow
+  // execution plan: plan[g] = entry count of group g, plan[groups] = the slot
+  // stride nq, group g's entries at plan + groups + 1 + g * nq
   const int ngroups = (nq + kPlanRows - 1) / kPlanRows;
   const int groups = bh * ngroups;
-  int32_t* gcounts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4) + al(rows * 4));
-  hipLaunchKernelGGL(group_count_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, ngroups, gcounts);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, gcounts, groups, plan, plan + groups);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, ngroups, plan,
                      plan + groups + 1);
   return hipGetLastError();

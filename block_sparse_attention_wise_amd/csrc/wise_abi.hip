@@ -248,8 +248,10 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
   // 16-token rows are bitmasks of 2048 blocks in both kernels' LDS
   if (block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
   if (plan != nullptr) {
-    const int64_t groups = (int64_t)batch * heads * ((seqlen / kBlock + kPlanRows - 1) / kPlanRows);
-    if (!aligned4(plan) || plan_capacity < groups + 1) return WISE_ERR_INVALID_ARG;
+    // every group's fixed slot must be readable
+    const int64_t bh = (int64_t)batch * heads;
+    const size_t need = bh <= INT32_MAX ? wise_build_support_plan_capacity((int)bh, seqlen / kBlock) : 0;
+    if (!aligned4(plan) || need == 0 || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
     // the fp32 kernel and 16-token schedules walk the CSR rows
     if (dt != WISE_BF16 || block != kBlock) plan = nullptr;
   }

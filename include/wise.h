@@ -118,7 +118,8 @@ size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
 /*
  * int32 entries of the optional execution plan wise_build_support can emit
  * beside the CSR schedule for bh rows of nq query blocks (0 on invalid sizes):
- * G + 1 + G*nq with G = bh * ceil(nq / 4) query-block groups.
+ * G + 1 + G*nq with G = bh * ceil(nq / 4) query-block groups (G entry
+ * counts, the slot stride, and a fixed slot of nq entries per group).
  */
 size_t wise_build_support_plan_capacity(int bh, int nq);
 
@@ -146,9 +147,11 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 prepares with the sparse schedule), with
  *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq).
  *                 Query blocks are taken in groups of 4 consecutive blocks of one
- *                 (batch, head); group g = bh_index*ceil(nq/4) + q/4.  plan[0..G]
- *                 are entry offsets (group g owns entries off[g] .. off[g+1]) and
- *                 the entries follow at plan + G + 1: each is
+ *                 (batch, head); group g = bh_index*ceil(nq/4) + q/4.  plan[g]
+ *                 (g < G) is group g's entry count n_g, plan[G] = nq the slot
+ *                 stride, and group g's entries are plan[G + 1 + g*nq ..
+ *                 G + g*nq + n_g] (a fixed slot, so a reader loads the count and
+ *                 the first entries at once); each entry is
  *                 (key block << 8) | membership, bit w of the membership set iff
  *                 query block 4*(g mod ceil(nq/4)) + w lists that key block.  Each
  *                 key block of the group's union appears once, in runs of 4 (the
@@ -253,12 +256,14 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  *   col_capacity           : number of readable col_idx entries.
  *   plan, plan_capacity    : NULL, or the execution plan wise_build_support wrote
  *                            for this same schedule, plan_capacity its readable
- *                            int32 entries (>= G + 1).  When given, the bf16
+ *                            int32 entries (at least
+ *                            wise_build_support_plan_capacity(batch*heads,
+ *                            seqlen / 32), else WISE_ERR_INVALID_ARG).  When given, the bf16
  *                            kernel walks the plan instead of the CSR rows (same
  *                            result up to the order of floating-point summation);
  *                            the fp32 kernel and block 16 ignore it.
- * Entries outside 0..q, and offsets outside 0..col_capacity (0..plan_capacity),
- * are ignored.  In the CSR a block listed twice counts once; a plan must come
+ * Entries outside 0..q, CSR offsets outside 0..col_capacity and plan entry
+ * counts outside 0..nq are ignored (clamped).  In the CSR a block listed twice counts once; a plan must come
  * from wise_build_support, which lists each block of a group once.  A row left
  * with no admissible key writes o = 0 and lse = -inf (wise_build_support never
  * produces one).  The bf16 kernel supports up to 4096 key blocks per head

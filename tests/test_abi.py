@@ -127,10 +127,10 @@ def test_workspace_bytes(lib):
     f = lib.wise_build_support_workspace_bytes
     assert f(0, 8, 4) == 0 and f(1, 0, 4) == 0 and f(1, 8, 0) == 0 and f(1, 8, 65) == 0
     assert f(1, 4097, 4) == 0
-    # bitmask words per row, one count per row and one per 4-block group, 256-byte aligned sections
+    # bitmask words per row and one count per row, 256-byte aligned sections
     def expect(bh, nq):
         al = lambda x: (x + 255) // 256 * 256
-        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4) + al(bh * ((nq + 3) // 4) * 4)
+        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4)
     for bh, nq in ((1, 8), (32, 128), (32, 512), (3, 33)):
         assert f(bh, nq, 4) == expect(bh, nq)
 
@@ -138,7 +138,7 @@ def test_workspace_bytes(lib):
 def test_plan_capacity(lib):
     f = lib.wise_build_support_plan_capacity
     assert f(0, 8) == 0 and f(1, 0) == 0 and f(1, 4097) == 0
-    # group offsets (G + 1) plus at most nq union blocks per group
+    # group entry counts and the slot stride (G + 1) plus a fixed slot of nq entries per group
     for bh, nq in ((1, 8), (32, 128), (3, 33), (1, 1)):
         g = bh * ((nq + 3) // 4)
         assert f(bh, nq) == g + 1 + g * nq
@@ -190,8 +190,10 @@ def test_sparse_validation(lib):
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
     assert sp(d=80) == UNSUPPORTED
-    assert sp(plan=P, pcap=1) == INVALID                # fewer than G + 1 = 2 entries
-    assert sp(plan=ctypes.c_void_p(0x10002), pcap=64) == INVALID
+    need = lib.wise_build_support_plan_capacity(1, 4)    # 1 group: counts, stride, 4 entry slots
+    assert need == 1 + 1 + 4
+    assert sp(plan=P, pcap=need - 1) == INVALID         # a group slot would be out of reach
+    assert sp(plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
 
 
 def test_variant_and_retained_validation(lib):
@@ -226,7 +228,7 @@ def test_blocked_builder_validation(lib):
     for bh, nq, steps, blk in ((2, 8, 4, 64), (3, 32, 4, 128), (1, 128, 1, 64)):
         fct = blk // 32
         nqb = nq // fct
-        base = al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4) + al(bh * ((nq + 3) // 4) * 4)
+        base = al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4)
         extra = al(steps * bh * nqb * nqb * 4) + al(bh * nqb * ((nqb + 31) // 32) * 4) + al(bh * nqb * 4)
         assert f(bh, nq, steps, blk) == base + extra
     assert f(2, 8, 4, 32) == lib.wise_build_support_workspace_bytes(2, 8, 4)

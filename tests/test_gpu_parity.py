@@ -326,13 +326,15 @@ def test_uniform_attention_closed_form_on_gpu():
 
 
 def _decode_plan(plan, bh, nq, rows_per_group=4):
-    """plan (host int32) -> {group: [(block, membership), ...]} in plan order."""
+    """plan (host int32) -> {group: [(block, membership), ...]} in plan order: entry
+    counts plan[0..G), the slot stride plan[G] = nq, group g's entries in its slot
+    plan[G + 1 + g nq ..]."""
     ng = (nq + rows_per_group - 1) // rows_per_group
     groups = bh * ng
-    off = plan[:groups + 1]
+    cnt = plan[:groups]
+    assert int(plan[groups]) == nq and np.all(cnt >= 0) and np.all(cnt <= nq)
     ent = plan[groups + 1:]
-    assert off[0] == 0 and np.all(np.diff(off) >= 0)
-    return {g: [(int(e) >> 8, int(e) & 255) for e in ent[off[g]:off[g + 1]]] for g in range(groups)}
+    return {g: [(int(e) >> 8, int(e) & 255) for e in ent[g * nq:g * nq + cnt[g]]] for g in range(groups)}
 
 
 @pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0)])
