@@ -252,21 +252,27 @@ static_assert(kPlanRows >= 1 && kPlanRows <= 8, "plan rows fit the 8-bit members
 static_assert(kPlanTrip >= 1 && kPlanTrip <= 16, "plan trip");
 constexpr int kMasks = 1 << kPlanRows;
 
-// one wavefront per group: collect (block, mask) tiles in ascending block order,
-// bucket them by mask (stable), then fill the trips greedily, every lane
-// scoring a quarter of the masks for each pick.  The group's entries go to its
-// fixed slot of nq entries and their number to counts[g], so a reader finds
-// both without a prefix sum (and can load them together); counts[groups] = nq.
+// one wavefront per group: load the rows' bitmask words at once, collect
+// (block, mask) tiles in ascending block order, bucket them by mask (a stable
+// counting sort, one ballot per mask value and chunk of 64 tiles), then fill
+// the trips greedily: lane m holds bucket m's remaining count, every lane scores
+// its mask, and a wave minimum picks one.  The group's entries go to its fixed
+// slot of nq entries and their number to counts[g], so a reader finds both
+// without a prefix sum (and can load them together); counts[groups] = nq.
+static_assert(kMasks <= 16, "one bucket per lane of the first 16-lane row");
 __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
                                                         int32_t* counts, int32_t* entries) {
+  __shared__ uint32_t wbuf[kPlanRows * (kMaxNq / 32)];
   __shared__ int32_t tiles[kMaxNq];
   __shared__ int32_t sorted_tiles[kMaxNq];
-  __shared__ int32_t bcount[kMasks], bstart[kMasks];
   const int g = blockIdx.x, lane = threadIdx.x;
   const int bh = g / ngroups, q0 = kPlanRows * (g - bh * ngroups);
-  const int qlast = min(q0 + kPlanRows, nq) - 1;
-  const int words = (qlast >> 5) + 1;
-  for (int m = lane; m < kMasks; m += 64) bcount[m] = 0;
+  const int nr = min(q0 + kPlanRows, nq) - q0;  // rows in the group
+  const int words = ((q0 + nr - 1) >> 5) + 1;   // words covering key blocks 0 .. last row
+  for (int x = lane; x < nr * words; x += 64) {
+    const int r = x / words, w = x - r * words;
+    wbuf[x] = masks[(size_t)(bh * nq + q0 + r) * nwords + w];
+  }
   __syncthreads();
   // ascending union tiles with their membership masks
   int n = 0;
@@ -274,34 +280,50 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
     const int b = 32 * w + (lane & 31);
     int m = 0;
     if (lane < 32) {
-      for (int r = q0; r <= qlast; ++r)
-        if ((masks[(size_t)(bh * nq + r) * nwords + w] >> (lane & 31)) & 1u) m |= 1 << (r - q0);
+      for (int r = 0; r < nr; ++r) m |= (int)((wbuf[r * words + w] >> lane) & 1u) << r;
     }
     const uint64_t present = __ballot(m != 0);
-    const int pos = n + __popcll(present & ((1ull << lane) - 1ull));
-    if (m != 0) {
-      tiles[pos] = (b << 8) | m;
-      atomicAdd(&bcount[m], 1);
-    }
+    if (m != 0) tiles[n + __popcll(present & ((1ull << lane) - 1ull))] = (b << 8) | m;
     n += __popcll(present);
   }
   __syncthreads();
-  if (lane == 0) {
-    int acc = 0;
-    for (int m = 0; m < kMasks; ++m) {
-      bstart[m] = acc;
-      acc += bcount[m];
-      bcount[m] = 0;
+  // bucket sizes (lane m: bucket m), then each tile's slot: its bucket's start
+  // plus the tiles of its bucket before it (stable)
+  int cnt = 0;
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int m = t0 + lane < n ? tiles[t0 + lane] & (kMasks - 1) : -1;
+#pragma unroll
+    for (int v = 0; v < kMasks; ++v) {
+      const int c = __popcll(__ballot(m == v));
+      if (lane == v) cnt += c;
     }
-    for (int t = 0; t < n; ++t) {  // stable: ascending blocks within a bucket
-      const int m = tiles[t] & (kMasks - 1);
-      sorted_tiles[bstart[m] + bcount[m]++] = tiles[t];
+  }
+  int start = cnt;  // exclusive prefix over the buckets
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(start, off);
+    if (lane >= off) start += y;
+  }
+  start -= cnt;
+  int fill = 0;  // lane m: tiles of bucket m placed so far
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    const int e = t < n ? tiles[t] : 0;
+    const int m = t < n ? e & (kMasks - 1) : -1;
+    int dst = 0;
+#pragma unroll
+    for (int v = 0; v < kMasks; ++v) {
+      const uint64_t bal = __ballot(m == v);
+      const int base = __shfl(start + fill, v);
+      if (m == v) dst = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == v) fill += __popcll(bal);
     }
+    if (t < n) sorted_tiles[dst] = e;
   }
   __syncthreads();
   int32_t* out = entries + (size_t)g * nq;  // the group's fixed slot of nq entries
   if (lane == 0) counts[g] = n;
   if (g == 0 && lane == 0) counts[gridDim.x] = nq;
+  int left = lane < kMasks ? cnt : 0;  // lane m: tiles of bucket m not yet placed
   int load[kPlanRows];
   for (int k = 0; k < n;) {
 #pragma unroll
@@ -309,19 +331,24 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
     for (int slot = 0; slot < kPlanTrip && k < n; ++slot) {
       // the mask whose tile raises the trip's busiest row the least; ties go to
       // the mask covering more rows (more work per trip), then the lower mask
-      int best = 0x7fffffff;
-      for (int m = 1 + lane; m < kMasks; m += 64) {
-        if (bcount[m] == 0) continue;
+      int key = 0x7fffffff;
+      if (lane >= 1 && lane < kMasks && left > 0) {
         int mx = 0;
 #pragma unroll
-        for (int w = 0; w < kPlanRows; ++w) mx = max(mx, load[w] + ((m >> w) & 1));
-        const int key = ((32 * mx - __popc(m) + 32) << 8) | m;
-        best = min(best, key);
+        for (int w = 0; w < kPlanRows; ++w) mx = max(mx, load[w] + ((lane >> w) & 1));
+        key = ((32 * mx - __popc(lane) + 32) << 8) | lane;
       }
-      for (int off = 32; off > 0; off >>= 1) best = min(best, __shfl_xor(best, off));
-      const int m = best & (kMasks - 1);
-      if (lane == 0) out[k] = sorted_tiles[bstart[m] + (--bcount[m])];
-      __syncthreads();
+      // minimum over lanes 0..15 (the masks), a prefix minimum by DPP row shifts
+      // that leaves it in lane 15
+      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x111, 0xF, 0xF, false));
+      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x112, 0xF, 0xF, false));
+      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x114, 0xF, 0xF, false));
+      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x118, 0xF, 0xF, false));
+      const int m = __builtin_amdgcn_readlane(key, 15) & (kMasks - 1);
+      // the bucket's last remaining tile (buckets drain from the top)
+      const int pos = __builtin_amdgcn_readlane(start + left - 1, m);
+      if (lane == m) --left;
+      if (lane == 0) out[k] = sorted_tiles[pos];
 #pragma unroll
       for (int w = 0; w < kPlanRows; ++w) load[w] += (m >> w) & 1;
       ++k;
