@@ -7,7 +7,9 @@
 //
 // Kernels:
 //   select_union  one 256-thread workgroup per (batch*head, query block) row.
-//                 For every step: the q+1 admissible masses are bitonic-sorted in
+//                 For every step (one step per wavefront, four at once, for rows
+//                 of up to 1024 blocks; the whole workgroup per step beyond): the
+//                 q+1 admissible masses are bitonic-sorted in
 //                 LDS by the 64-bit key (mass desc, index asc); an exclusive fp64
 //                 prefix sum over the sorted masses marks block k as selected iff
 //                 the mass before it is still below eta; selected blocks are ORed
@@ -75,6 +77,17 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double* wsum, i
   return base + inc - x;
 }
 
+// Rows of at most kWaveSortMax admissible blocks take one step per wavefront:
+// the four wavefronts sort and scan four steps' masses at once, each in its own
+// quarter of the key buffer, synchronising only within the wavefront.
+constexpr int kWaveSortMax = kMaxNq / (kSelThreads / 64);
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a) {
   __shared__ uint64_t keys[kMaxNq];
   __shared__ uint32_t uni[kMaxNq / 32];
@@ -107,65 +120,115 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a
     for (int w = 0; w < a.nwords; ++w) ref_count += __popc(refm[w]);
   }
 
-  for (int t = 0; t < a.steps; ++t) {
-    const float* mrow = a.mass + (((size_t)t * a.bh + bh) * a.nq + qb) * (size_t)a.nq;
-    __syncthreads();
-    for (int e = tid; e < n2; e += kSelThreads)
-      keys[e] = e < n ? ((uint64_t)ordered_bits(mrow[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
-    __syncthreads();
-    // bitonic sort, descending
-    for (int size = 2; size <= n2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int e = tid; e < (n2 >> 1); e += kSelThreads) {
-          const int lo = 2 * e - (e & (stride - 1));
-          const int hi = lo + stride;
-          const bool desc = (lo & size) == 0;
-          const uint64_t x = keys[lo], y = keys[hi];
-          if ((x < y) == desc) {
-            keys[lo] = y;
-            keys[hi] = x;
+  if (a.kind == kCumulative && n2 <= kWaveSortMax) {
+    __syncthreads();  // uni cleared
+    const int wave = tid >> 6, lane = tid & 63;
+    uint64_t* kw = keys + wave * kWaveSortMax;
+    for (int t = wave; t < a.steps; t += kSelThreads / 64) {
+      const float* mrow = a.mass + (((size_t)t * a.bh + bh) * a.nq + qb) * (size_t)a.nq;
+      for (int e = lane; e < n2; e += 64)
+        kw[e] = e < n ? ((uint64_t)ordered_bits(mrow[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+      wave_sync();
+      // bitonic sort, descending
+      for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int e = lane; e < (n2 >> 1); e += 64) {
+            const int lo = 2 * e - (e & (stride - 1));
+            const int hi = lo + stride;
+            const bool desc = (lo & size) == 0;
+            const uint64_t x = kw[lo], y = kw[hi];
+            if ((x < y) == desc) {
+              kw[lo] = y;
+              kw[hi] = x;
+            }
           }
+          wave_sync();
         }
+      }
+      // exclusive fp64 prefix over the sorted masses; each lane owns a contiguous chunk
+      const int per = (n + 63) / 64;
+      const int c0 = lane * per;
+      const int c1 = min(n, c0 + per);
+      double local = 0.0;
+      for (int e = c0; e < c1; ++e) local += (double)from_ordered_bits((uint32_t)(kw[e] >> 32));
+      double inc = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+      }
+      double run = inc - local;
+      for (int e = c0; e < c1; ++e) {
+        const uint64_t key = kw[e];
+        if (a.eta >= 1.0 || run < a.eta) {
+          const uint32_t b = 0xffffffffu - (uint32_t)(key & 0xffffffffu);
+          atomicOr(&uni[b >> 5], 1u << (b & 31));
+        }
+        run += (double)from_ordered_bits((uint32_t)(key >> 32));
+      }
+      wave_sync();  // the next step reuses this wavefront's keys
+    }
+  } else {
+    for (int t = 0; t < a.steps; ++t) {
+      const float* mrow = a.mass + (((size_t)t * a.bh + bh) * a.nq + qb) * (size_t)a.nq;
+      __syncthreads();
+      for (int e = tid; e < n2; e += kSelThreads)
+        keys[e] = e < n ? ((uint64_t)ordered_bits(mrow[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+      __syncthreads();
+      // bitonic sort, descending
+      for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int e = tid; e < (n2 >> 1); e += kSelThreads) {
+            const int lo = 2 * e - (e & (stride - 1));
+            const int hi = lo + stride;
+            const bool desc = (lo & size) == 0;
+            const uint64_t x = keys[lo], y = keys[hi];
+            if ((x < y) == desc) {
+              keys[lo] = y;
+              keys[hi] = x;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      // exclusive fp64 prefix over the sorted masses; each thread owns a contiguous chunk
+      const int per = (n + kSelThreads - 1) / kSelThreads;
+      const int c0 = tid * per;
+      const int c1 = min(n, c0 + per);
+      double local = 0.0, local_ref = 0.0;
+      for (int e = c0; e < c1; ++e) {
+        const double m = (double)from_ordered_bits((uint32_t)(keys[e] >> 32));
+        local += m;
+        if (a.kind == kMassMatched) {
+          const uint32_t b = 0xffffffffu - (uint32_t)(keys[e] & 0xffffffffu);
+          if ((refm[b >> 5] >> (b & 31)) & 1u) local_ref += m;
+        }
+      }
+      double run = block_exclusive_scan(local, wsum, tid);
+      double thr = a.eta;
+      if (a.kind == kMassMatched) {
+        // the reference row's mass, summed in the same sorted order and chunking
+        const double ref_excl = block_exclusive_scan(local_ref, wsum, tid);
+        if (tid == kSelThreads - 1) wsum[0] = ref_excl + local_ref;
+        __syncthreads();
+        thr = wsum[0] - kMassMatchSlack;
         __syncthreads();
       }
-    }
-    // exclusive fp64 prefix over the sorted masses; each thread owns a contiguous chunk
-    const int per = (n + kSelThreads - 1) / kSelThreads;
-    const int c0 = tid * per;
-    const int c1 = min(n, c0 + per);
-    double local = 0.0, local_ref = 0.0;
-    for (int e = c0; e < c1; ++e) {
-      const double m = (double)from_ordered_bits((uint32_t)(keys[e] >> 32));
-      local += m;
-      if (a.kind == kMassMatched) {
-        const uint32_t b = 0xffffffffu - (uint32_t)(keys[e] & 0xffffffffu);
-        if ((refm[b >> 5] >> (b & 31)) & 1u) local_ref += m;
+      for (int e = c0; e < c1; ++e) {
+        const uint64_t key = keys[e];
+        bool take;
+        if (a.kind == kSizeMatched)
+          take = e < ref_count;
+        else if (a.kind == kMassMatched)
+          take = e == 0 || run < thr;
+        else
+          take = a.eta >= 1.0 || run < a.eta;
+        if (take) {
+          const uint32_t b = 0xffffffffu - (uint32_t)(key & 0xffffffffu);
+          atomicOr(&uni[b >> 5], 1u << (b & 31));
+        }
+        run += (double)from_ordered_bits((uint32_t)(key >> 32));
       }
-    }
-    double run = block_exclusive_scan(local, wsum, tid);
-    double thr = a.eta;
-    if (a.kind == kMassMatched) {
-      // the reference row's mass, summed in the same sorted order and chunking
-      const double ref_excl = block_exclusive_scan(local_ref, wsum, tid);
-      if (tid == kSelThreads - 1) wsum[0] = ref_excl + local_ref;
-      __syncthreads();
-      thr = wsum[0] - kMassMatchSlack;
-      __syncthreads();
-    }
-    for (int e = c0; e < c1; ++e) {
-      const uint64_t key = keys[e];
-      bool take;
-      if (a.kind == kSizeMatched)
-        take = e < ref_count;
-      else if (a.kind == kMassMatched)
-        take = e == 0 || run < thr;
-      else
-        take = a.eta >= 1.0 || run < a.eta;
-      if (take) {
-        const uint32_t b = 0xffffffffu - (uint32_t)(key & 0xffffffffu);
-        atomicOr(&uni[b >> 5], 1u << (b & 31));
-      }
-      run += (double)from_ordered_bits((uint32_t)(key >> 32));
     }
   }
   __syncthreads();
