@@ -778,14 +778,23 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
 // Two workgroups per CU (two wavefronts per SIMD, up to 256 VGPRs each): the
 // two-block softmax steps need the registers, and the sparse mode's four
 // register staging sets and LDS tiles per trip too.
+// Workgroups per CU (= wavefronts per SIMD): three where the kernel fits in 168
+// VGPRs without spilling (d = 64 throughout; dense d = 96) and the LDS tiles of
+// three workgroups fit, else two.
 template <int D, int MODE>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_dense_kernel(
-    AttnBf16Args a) {
+constexpr int stream_occupancy() {
+  if (D == 64) return 3;
+  if (D == 96 && MODE == kDense) return 3;
+  return 2;
+}
+template <int D, int MODE>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((
+    amdgpu_waves_per_eu(stream_occupancy<D, MODE>(), stream_occupancy<D, MODE>()))) void attn_dense_kernel(AttnBf16Args a) {
   attn_stream<D, MODE>(a);
 }
 template <int D, int MODE>
-__global__ __launch_bounds__(64 * kSparseWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_sparse_kernel(
-    AttnBf16Args a) {
+__global__ __launch_bounds__(64 * kSparseWaves) __attribute__((
+    amdgpu_waves_per_eu(stream_occupancy<D, MODE>(), stream_occupancy<D, MODE>()))) void attn_sparse_kernel(AttnBf16Args a) {
   attn_stream<D, MODE>(a);
 }
 
