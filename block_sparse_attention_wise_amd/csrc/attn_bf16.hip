@@ -281,7 +281,7 @@ __device__ __forceinline__ float finish_rows(const RowState<D>& st, __bf16* orow
 // sparse union reads each shared block once per workgroup.  Global loads run one
 // trip ahead of the compute through register staging sets.
 
-constexpr int kWaves = 4;       // dense workgroups
+constexpr int kWaves = 4;       // four-row workgroups
 constexpr int kSparseWaves = kPlanRows;  // sparse workgroups
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left free
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
@@ -292,6 +292,27 @@ constexpr int kEntryShift = 8;      // list entries: (block << 8) | row mask
 // kDenseMass16 / kSparse16: the block mass and the schedule at 16-token blocks
 enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2, kDenseMass16 = 3, kSparse16 = 4 };
 constexpr int kSparseTrip = kPlanTrip;  // tiles per trip of the sparse kernel
+
+// Wavefronts per SIMD (two, up to 256 VGPRs each: the two-block softmax steps,
+// and the sparse modes' four staging sets, need the registers), three where a
+// kernel fits 168 VGPRs without spilling and three workgroups' LDS tiles fit a
+// CU: every mode at d = 64, the dense mode at d = 96.
+template <int D, int MODE>
+constexpr int stream_occupancy() {
+  if (D == 64) return 3;
+  if (D == 96 && MODE == kDense) return 3;
+  return 2;
+}
+// Wavefronts (= query blocks) per workgroup.  The sparse modes take four rows,
+// the unit their trips are balanced over.  The dense modes take four rows where
+// three workgroups share a CU, else eight: one eight-wavefront workgroup per CU
+// at the same wavefronts per SIMD, whose eight rows share every tile copy (half
+// the tile loads and LDS stores per row-step of two four-row workgroups).
+template <int D, int MODE>
+constexpr int stream_waves() {
+  if (MODE == kSparse || MODE == kSparse16) return kSparseWaves;
+  return stream_occupancy<D, MODE>() == 3 ? kWaves : 2 * kWaves;
+}
 
 // Key-block lists.  next() is wave-uniform (scalar) control flow and returns an
 // entry (block << 8) | mask, bit w of mask set when wavefront w's row takes the
@@ -362,7 +383,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   constexpr bool SUB = MODE == kSparse16;
   constexpr bool MASS = MODE == kDenseMass || MODE == kDenseMass16;
   constexpr int BL = MODE == kDenseMass ? 32 : MODE == kDenseMass16 ? 16 : 0;  // one-pass block-mass store
-  constexpr int W = SPARSE ? kSparseWaves : kWaves;  // wavefronts = query blocks per workgroup
+  constexpr int W = stream_waves<D, MODE>();  // wavefronts = query blocks per workgroup
   constexpr int NTHR = 64 * W;
   constexpr int CHUNKS = 32 * T::C8;                // 16-byte chunks of one tile
   constexpr int CPT = (CHUNKS + NTHR - 1) / NTHR;  // ... per thread
@@ -775,20 +796,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   }
 }
 
-// Two workgroups per CU (two wavefronts per SIMD, up to 256 VGPRs each): the
-// two-block softmax steps need the registers, and the sparse mode's four
-// register staging sets and LDS tiles per trip too.
-// Workgroups per CU (= wavefronts per SIMD): three where the kernel fits in 168
-// VGPRs without spilling (d = 64 throughout; dense d = 96) and the LDS tiles of
-// three workgroups fit, else two.
 template <int D, int MODE>
-constexpr int stream_occupancy() {
-  if (D == 64) return 3;
-  if (D == 96 && MODE == kDense) return 3;
-  return 2;
-}
-template <int D, int MODE>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((
+__global__ __launch_bounds__((64 * stream_waves<D, MODE>())) __attribute__((
     amdgpu_waves_per_eu(stream_occupancy<D, MODE>(), stream_occupancy<D, MODE>()))) void attn_dense_kernel(AttnBf16Args a) {
   attn_stream<D, MODE>(a);
 }
@@ -800,23 +809,31 @@ __global__ __launch_bounds__(64 * kSparseWaves) __attribute__((
 
 // ------------------------------------------------------------------ launch
 
+template <int D, int MODE>
+static void launch_mode(const AttnBf16Args& a, hipStream_t stream) {
+  constexpr int w = stream_waves<D, MODE>();
+  const int bhn = a.rows / a.nq;
+  const dim3 grid(bhn * ((a.nq + w - 1) / w)), block(64 * w);
+  if constexpr (MODE == kSparse || MODE == kSparse16)
+    hipLaunchKernelGGL((attn_sparse_kernel<D, MODE>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_dense_kernel<D, MODE>), grid, block, 0, stream, a);
+}
+
 template <int D>
 static void launch_d(const AttnBf16Args& a, bool sparse, bool mass, bool b16, hipStream_t stream) {
-  const int bhn = a.rows / a.nq;
-  const int w = sparse ? kSparseWaves : kWaves;
-  const dim3 grid(bhn * ((a.nq + w - 1) / w)), block(64 * w);
   if (sparse) {
     if (b16)
-      hipLaunchKernelGGL((attn_sparse_kernel<D, kSparse16>), grid, block, 0, stream, a);
+      launch_mode<D, kSparse16>(a, stream);
     else
-      hipLaunchKernelGGL((attn_sparse_kernel<D, kSparse>), grid, block, 0, stream, a);
+      launch_mode<D, kSparse>(a, stream);
   } else if (mass) {
     if (b16)
-      hipLaunchKernelGGL((attn_dense_kernel<D, kDenseMass16>), grid, block, 0, stream, a);
+      launch_mode<D, kDenseMass16>(a, stream);
     else
-      hipLaunchKernelGGL((attn_dense_kernel<D, kDenseMass>), grid, block, 0, stream, a);
+      launch_mode<D, kDenseMass>(a, stream);
   } else {
-    hipLaunchKernelGGL((attn_dense_kernel<D, kDense>), grid, block, 0, stream, a);
+    launch_mode<D, kDense>(a, stream);
   }
 }
 
