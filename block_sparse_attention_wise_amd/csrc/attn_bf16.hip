@@ -520,7 +520,11 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       }
     }
   };
-  auto member = [&](int e) -> bool { return active && ((e >> wave) & 1) && (e >> kEntryShift) <= qb; };
+  // an entry's row mask has kEntryShift bits; the dense lists hold every row
+  static_assert(!SPARSE || W <= kEntryShift, "row mask width");
+  auto member = [&](int e) -> bool {
+    return active && (!SPARSE || ((e >> wave) & 1)) && (e >> kEntryShift) <= qb;
+  };
 
   // Runs `work(entries)` over the list, TRIP blocks per trip: the trip's
   // tiles sit in LDS buffers 0..TRIP-1 while the next trip's are fetched into
