@@ -269,10 +269,12 @@ __device__ __forceinline__ float finish_rows(const RowState<D>& st, __bf16* orow
 // (batch, head); wavefront w owns query block q0 + w.  The workgroup streams a
 // list of key blocks through LDS tiles shared by its wavefronts, TRIP tiles per
 // trip, and every wavefront runs the key-block step on the blocks of its own row:
-//   dense   (W = 4, TRIP = 2) list = 0 .. q0+3, wavefront w takes b <= q0 + w;
+//   dense   (W = 4 or 8, TRIP = 2) list = 0 .. q0+W-1, wavefront w takes b <= q0 + w;
 //   sparse  (W = 4, TRIP = 4) list = union of the 4 rows' scheduled blocks (the
 //           execution plan's order, else ascending), wavefront w takes the
-//           blocks of its own row;
+//           blocks of its own row; with an execution plan the group's rows are
+//           the plan's (rows of similar length, not necessarily consecutive)
+//           and wavefront w owns the group's row w;
 //   16-token blocks: a wavefront's 32 queries are two 16-token query blocks; the
 //           block mass is summed per 16 x 16 sub-block of each tile, and the
 //           sparse list walks the 32-key tiles holding any scheduled 16-token key
@@ -419,11 +421,32 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // and the query heads of one key-value group share that XCD's L2.
   const int slot = blockIdx.x % bhn;
   const int bh = (bhn & 7) == 0 ? (slot & 7) * (bhn >> 3) + (slot >> 3) : slot;
-  const int grp = ngroups - 1 - (int)(blockIdx.x / bhn);
-  const int q0 = W * grp;
-  const int qb = q0 + wave;
-  const bool active = qb < a.nq;
-  const int qlast = min(q0 + W, a.nq) - 1;
+  constexpr bool PLAN_ROWS = SPARSE && !SUB;  // rows may come from an execution plan
+  const bool use_plan = PLAN_ROWS && a.plan != nullptr;
+  int qb, qlast, pgroup = 0;
+  if (use_plan) {
+    // the plan's groups of this head come longest first: workgroup p takes the
+    // (p / bhn)-th; its rows are listed first, -1 after (rows outside 0..nq-1
+    // are ignored)
+    const int gh = plan_groups_per_head(a.nq);
+    pgroup = bh * gh + (int)(blockIdx.x / bhn);
+    const int32_t* gr = a.plan + bhn * gh + 1 + (size_t)kPlanRows * pgroup;
+    qb = -1;
+    qlast = -1;
+#pragma unroll
+    for (int w = 0; w < kPlanRows; ++w) {
+      int r = gr[w];
+      r = r >= 0 && r < a.nq ? r : -1;
+      if (w == wave) qb = r;
+      qlast = max(qlast, r);
+    }
+    if (qlast < 0) return;  // an empty group (uniform over the workgroup)
+  } else {
+    const int grp = ngroups - 1 - (int)(blockIdx.x / bhn);
+    qb = W * grp + wave;
+    qlast = min(W * grp + W, a.nq) - 1;
+  }
+  const bool active = qb >= 0 && qb < a.nq;
   const size_t head_off = (size_t)bh * a.seqlen * D;
   // grouped-query attention: query head h of batch b reads key-value head
   // b * (heads / kv_group) + h / kv_group
@@ -436,14 +459,14 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // and discard it, so the load is unconditional and completes before the loop
   // (keeping the in-loop waits on the prefetched K/V tiles only).
   QRegs<D> qf;
-  load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * min(qb, a.nq - 1) + i) * D, h);
+  load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * (active ? qb : qlast) + i) * D, h);
   // sparse mode with an execution plan: group g's entry count plan[g] and its
   // first entries (fixed slot of nq entries) load together with Q
   PlanList plist{nullptr, 0, 0, qlast, lane, -1, 64};
-  if (SPARSE && !SUB && a.plan != nullptr) {
-    const int groups = bhn * ngroups, g = bh * ngroups + grp;
+  if (use_plan) {
+    const int groups = bhn * plan_groups_per_head(a.nq), g = pgroup;
     const int slot = g * a.nq;  // plan capacity (checked on the host) covers every slot
-    plist.e = a.plan + groups + 1;
+    plist.e = a.plan + groups + 1 + kPlanRows * groups;
     plist.base = slot;
     plist.load_chunk(slot + a.nq);
     const int cnt = a.plan[g];
@@ -608,7 +631,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
                                             blse, bi);
     }
   };
-  if (SPARSE && !SUB && a.plan != nullptr) {
+  if (use_plan) {
     stream(plist, true, attend);
   } else if (SPARSE) {
     UnionList<W> list{rmask, (qlast >> 5) + 1, 0, 0u};
@@ -817,7 +840,8 @@ template <int D, int MODE>
 static void launch_mode(const AttnBf16Args& a, hipStream_t stream) {
   constexpr int w = stream_waves<D, MODE>();
   const int bhn = a.rows / a.nq;
-  const dim3 grid(bhn * ((a.nq + w - 1) / w)), block(64 * w);
+  const int per_head = MODE == kSparse && a.plan != nullptr ? plan_groups_per_head(a.nq) : (a.nq + w - 1) / w;
+  const dim3 grid(bhn * per_head), block(64 * w);
   if constexpr (MODE == kSparse || MODE == kSparse16)
     hipLaunchKernelGGL((attn_sparse_kernel<D, MODE>), grid, block, 0, stream, a);
   else

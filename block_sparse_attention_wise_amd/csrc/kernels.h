@@ -7,10 +7,16 @@
 
 namespace wise {
 
-// The bf16 sparse kernel's workgroups own kPlanRows consecutive query blocks of
-// one head and hold kPlanTrip tiles per trip; the execution plan is built for both.
+// The bf16 sparse kernel's workgroups own up to kPlanRows query blocks of one
+// head and hold kPlanTrip tiles per trip; the execution plan is built for both.
+// With a plan, a head's rows are dealt to plan_groups_per_head(nq) groups (some
+// may stay empty); without one, to ceil(nq / kPlanRows) groups of consecutive
+// rows.
 constexpr int kPlanRows = 4;
 constexpr int kPlanTrip = 4;
+__host__ __device__ constexpr int plan_groups_per_head(int nq) {
+  return (nq + kPlanRows - 1) / kPlanRows + (nq + 15) / 16;
+}
 
 struct AttnBf16Args {
   const __bf16* q;

@@ -24,6 +24,9 @@
 //                 nnz.
 //   emit_csr      one wavefront per row: expands the bitmask into ascending
 //                 col_idx entries at row_ptr[row].
+//   group_rows    one workgroup per head: groups the head's rows for the sparse
+//                 kernel (execution plan).
+//   group_plan    one wavefront per group: the group's union tiles in trips.
 #include "common.h"
 #include "kernels.h"
 
@@ -247,14 +250,22 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a
 
 constexpr int kScanThreads = 1024;
 
+// also writes the largest row count to *max_count
 __global__ __launch_bounds__(kScanThreads) void scan_counts_kernel(const int32_t* counts, int rows,
-                                                                    int32_t* row_ptr, int32_t* nnz) {
+                                                                    int32_t* row_ptr, int32_t* nnz,
+                                                                    int32_t* max_count) {
   __shared__ int32_t wtot[kScanThreads / 64];
+  __shared__ int32_t wmax[kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (rows + kScanThreads - 1) / kScanThreads;
   const int c0 = tid * per, c1 = min(rows, c0 + per);
-  int local = 0;
-  for (int e = c0; e < c1; ++e) local += counts[e];
+  int local = 0, mx = 0;
+  for (int e = c0; e < c1; ++e) {
+    local += counts[e];
+    mx = max(mx, counts[e]);
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if (lane == 0) wmax[w] = mx;
   int inc = local;
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(inc, off);
@@ -272,6 +283,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_counts_kernel(const int32_t
   if (tid == kScanThreads - 1) {
     row_ptr[rows] = run;
     *nnz = run;
+  }
+  if (tid == 0) {
+    int m = 0;
+    for (int k = 0; k < kScanThreads / 64; ++k) m = max(m, wmax[k]);
+    *max_count = m;
   }
 }
 
@@ -302,9 +318,9 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
 
 // ---------------------------------------------------------------- execution plan
 //
-// Groups of kPlanRows consecutive query blocks of one head are the sparse
+// Groups of up to kPlanRows query blocks (rows) of one head are the sparse
 // kernel's work units.  A group's plan lists the union of its rows' key blocks,
-// each entry (block << 8) | membership mask (bit w: row q0 + w schedules it),
+// each entry (block << 8) | membership mask (bit w: the group's row w schedules it),
 // ordered in trips of kPlanTrip tiles (the tiles the kernel holds in LDS at
 // once, between two barriers) so that the rows' blocks spread evenly over the
 // trips: a trip lasts as long as its busiest row, so each trip is filled
@@ -315,6 +331,140 @@ static_assert(kPlanRows >= 1 && kPlanRows <= 8, "plan rows fit the 8-bit members
 static_assert(kPlanTrip >= 1 && kPlanTrip <= 16, "plan trip");
 constexpr int kMasks = 1 << kPlanRows;
 
+// Which rows share a group.  A group's workgroup runs one trip per kPlanTrip
+// tiles of its rows' union, and each trip lasts as long as its busiest row, so a
+// group of u union tiles whose longest row has m tiles costs about
+// kTripCost * ceil(u / kPlanTrip) + kTileCost * m: the per-trip loads, stores
+// and barriers against one softmax step per tile of the busiest row (weights in
+// the proportion measured for the 4k late step, 1.85 and 0.80 us).  Rows of
+// similar length waste the least time at the trip barriers, so each head's rows
+// are taken longest first (ties: lower index first) and packed greedily, up to
+// kPlanRows per group.  A group is closed early when the next row would push its
+// cost above 5/4 of that of the longest row of the whole schedule on its own:
+// the kernel cannot end before that row's group does, and much longer groups
+// would only lengthen the tail (measured on the 4k, Huginn and Llama
+// geometries: caps of 1 and 0.9 split too many groups at head_dim 128, no cap
+// leaves the tail long at head_dim 64; 5/4 is best at 128 and 96, neutral at
+// 64).  A head has at most plan_groups_per_head(nq) groups: once
+// the rows left would not fit in the groups left, groups are only closed when
+// full.  Groups come out longest first, the order the sparse kernel launches
+// them in; unused groups list no rows (-1).
+constexpr int kTripCost = 9, kTileCost = 4;
+constexpr int kCapNum = 5, kCapDen = 4;
+constexpr int kGroupThreads = 256;
+constexpr int kGroupChunk = 64;  // rows whose bitmasks are staged in LDS at once
+static_assert(kMaxNq <= 4096 && kMaxNq / 32 <= 128, "sort key and two union words per lane");
+
+__device__ __forceinline__ int group_cost(int u, int m) {
+  return kTripCost * ((u + kPlanTrip - 1) / kPlanTrip) + kTileCost * m;
+}
+
+// sum over the wavefront, in lane 63 (DPP row shifts, then row broadcasts)
+__device__ __forceinline__ int wave_sum_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_t* masks, const int32_t* counts,
+                                                                   const int32_t* max_count, int nq, int nwords,
+                                                                   int gh, int32_t* rows) {
+  __shared__ uint32_t keys[kMaxNq];
+  __shared__ uint32_t stage[kGroupChunk * (kMaxNq / 32)];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int32_t* cnt = counts + (size_t)h * nq;
+  // sort keys (count descending, row ascending), bitonic over a power of two
+  int n2 = 1;
+  while (n2 < nq) n2 <<= 1;
+  for (int q = tid; q < n2; q += kGroupThreads) {
+    const int c = q < nq ? min(max(cnt[q], 0), nq) : 0;
+    keys[q] = q < nq ? ((uint32_t)(kMaxNq - c) << 12) | (uint32_t)q : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += kGroupThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t x = keys[i], y = keys[l];
+          if ((x > y) == ((i & k) == 0)) {
+            keys[i] = y;
+            keys[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const int mc = min(max(*max_count, 0), nq);
+  const int cap = group_cost(mc, mc) * kCapNum / kCapDen;
+  int32_t* out = rows + (size_t)h * gh * kPlanRows;
+  // wavefront 0 packs the rows in order: the open group's union bitmask (words
+  // lane and lane + 64), the sum of its rows' counts (a bound on the union), its
+  // longest row m, its size, and its rows (lane s: row s).  The exact union size
+  // (a wavefront reduction) is only needed when the bound exceeds the cap.
+  uint32_t u0 = 0u, u1 = 0u;
+  int sum = 0, m = 0, gsize = 0, ng = 0, my_row = -1;
+  for (int c0 = 0; c0 < nq; c0 += kGroupChunk) {
+    const int nc = min(kGroupChunk, nq - c0);
+    __syncthreads();  // the previous chunk is consumed
+    for (int x = tid; x < nc * nwords; x += kGroupThreads) {
+      const int r = x / nwords, w = x - r * nwords;
+      const int q = (int)(keys[c0 + r] & 0xFFFu);
+      stage[x] = masks[((size_t)h * nq + q) * nwords + w];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // row r's key and mask words, fetched one row ahead
+      uint32_t nkey = keys[c0];
+      uint32_t nw0 = lane < nwords ? stage[lane] : 0u;
+      uint32_t nw1 = lane + 64 < nwords ? stage[lane + 64] : 0u;
+      for (int r = 0; r < nc; ++r) {
+        const uint32_t key = __builtin_amdgcn_readfirstlane(nkey), w0 = nw0, w1 = nw1;
+        if (r + 1 < nc) {
+          nkey = keys[c0 + r + 1];
+          nw0 = lane < nwords ? stage[(r + 1) * nwords + lane] : 0u;
+          nw1 = lane + 64 < nwords ? stage[(r + 1) * nwords + lane + 64] : 0u;
+        }
+        const int q = (int)(key & 0xFFFu), cq = kMaxNq - (int)(key >> 12);
+        const int left = nq - (c0 + r);  // rows not yet placed, this one included
+        bool close = gsize == kPlanRows;
+        if (!close && gsize > 0 && group_cost(sum + cq, max(m, cq)) > cap &&
+            ng + 1 + (left + kPlanRows - 1) / kPlanRows <= gh) {
+          const int u = wave_sum_dpp(__popc(u0 | w0) + __popc(u1 | w1));
+          close = group_cost(u, max(m, cq)) > cap;
+        }
+        if (close) {
+          if (lane < kPlanRows) out[ng * kPlanRows + lane] = lane < gsize ? my_row : -1;
+          ++ng;
+          gsize = 0;
+          u0 = w0;
+          u1 = w1;
+          sum = cq;
+          m = cq;
+        } else {
+          u0 |= w0;
+          u1 |= w1;
+          sum += cq;
+          m = max(m, cq);
+        }
+        if (lane == gsize) my_row = q;
+        ++gsize;
+      }
+    }
+  }
+  if (tid < 64) {
+    if (gsize > 0) {
+      if (lane < kPlanRows) out[ng * kPlanRows + lane] = lane < gsize ? my_row : -1;
+      ++ng;
+    }
+    for (int x = ng * kPlanRows + lane; x < gh * kPlanRows; x += 64) out[x] = -1;
+  }
+}
+
 // one wavefront per group: load the rows' bitmask words at once, collect
 // (block, mask) tiles in ascending block order, bucket them by mask (a stable
 // counting sort, one ballot per mask value and chunk of 64 tiles), then fill
@@ -323,18 +473,35 @@ constexpr int kMasks = 1 << kPlanRows;
 // slot of nq entries and their number to counts[g], so a reader finds both
 // without a prefix sum (and can load them together); counts[groups] = nq.
 static_assert(kMasks <= 16, "one bucket per lane of the first 16-lane row");
-__global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int ngroups,
-                                                        int32_t* counts, int32_t* entries) {
+__global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int gh,
+                                                        const int32_t* rows, int32_t* counts, int32_t* entries) {
   __shared__ uint32_t wbuf[kPlanRows * (kMaxNq / 32)];
   __shared__ int32_t tiles[kMaxNq];
   __shared__ int32_t sorted_tiles[kMaxNq];
   const int g = blockIdx.x, lane = threadIdx.x;
-  const int bh = g / ngroups, q0 = kPlanRows * (g - bh * ngroups);
-  const int nr = min(q0 + kPlanRows, nq) - q0;  // rows in the group
-  const int words = ((q0 + nr - 1) >> 5) + 1;   // words covering key blocks 0 .. last row
+  const int bh = g / gh;
+  if (g == 0 && lane == 0) counts[gridDim.x] = nq;
+  // the group's rows (valid ones first, -1 after)
+  int rq[kPlanRows], nr = 0, qlast = -1;
+#pragma unroll
+  for (int r = 0; r < kPlanRows; ++r) {
+    const int x = rows[(size_t)g * kPlanRows + r];
+    rq[r] = x >= 0 && x < nq ? x : -1;
+    if (rq[r] >= 0 && nr == r) ++nr;
+    qlast = max(qlast, rq[r]);
+  }
+  if (nr == 0) {
+    if (lane == 0) counts[g] = 0;
+    return;
+  }
+  const int words = (qlast >> 5) + 1;  // words covering key blocks 0 .. the last row
   for (int x = lane; x < nr * words; x += 64) {
     const int r = x / words, w = x - r * words;
-    wbuf[x] = masks[(size_t)(bh * nq + q0 + r) * nwords + w];
+    int q = rq[0];
+#pragma unroll
+    for (int s = 1; s < kPlanRows; ++s)
+      if (r == s) q = rq[s];
+    wbuf[x] = masks[(size_t)(bh * nq + q) * nwords + w];
   }
   __syncthreads();
   // ascending union tiles with their membership masks
@@ -385,7 +552,6 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
   __syncthreads();
   int32_t* out = entries + (size_t)g * nq;  // the group's fixed slot of nq entries
   if (lane == 0) counts[g] = n;
-  if (g == 0 && lane == 0) counts[gridDim.x] = nq;
   int left = lane < kMasks ? cnt : 0;  // lane m: tiles of bucket m not yet placed
   int load[kPlanRows];
   for (int k = 0; k < n;) {
@@ -420,15 +586,15 @@ __global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, i
 }
 
 size_t plan_capacity(int bh, int nq) {
-  const size_t groups = (size_t)bh * ((nq + kPlanRows - 1) / kPlanRows);
-  return groups + 1 + groups * (size_t)nq;
+  const size_t groups = (size_t)bh * plan_groups_per_head(nq);
+  return groups + 1 + groups * kPlanRows + groups * (size_t)nq;
 }
 
 size_t support_workspace_bytes(int bh, int nq) {
   const size_t rows = (size_t)bh * nq;
   const size_t nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al(rows * nwords * 4) + al(rows * 4);
+  return al(rows * nwords * 4) + al(rows * 4) + al(4);
 }
 
 // retained[row] = sum of mass[row][b] over the row's distinct scheduled blocks
@@ -477,18 +643,26 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   uint32_t* masks = static_cast<uint32_t*>(workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4));
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, (int)rows, row_ptr, nnz);
+  int32_t* max_count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + al(rows * nwords * 4) + al(rows * 4));
+  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, (int)rows, row_ptr, nnz,
+                     max_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, masks, nwords, row_ptr, col_idx);
   e = hipGetLastError();
   if (e != hipSuccess || plan == nullptr) return e;
   // execution plan: plan[g] = entry count of group g, plan[groups] = the slot
-  // stride nq, group g's entries at plan + groups + 1 + g * nq
-  const int ngroups = (nq + kPlanRows - 1) / kPlanRows;
-  const int groups = bh * ngroups;
-  hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, ngroups, plan,
-                     plan + groups + 1);
+  // stride nq, group g's rows at plan + groups + 1 + kPlanRows * g, its entries
+  // at plan + groups + 1 + kPlanRows * groups + g * nq
+  const int gh = plan_groups_per_head(nq);
+  const int groups = bh * gh;
+  int32_t* plan_rows = plan + groups + 1;
+  hipLaunchKernelGGL(group_rows_kernel, dim3(bh), dim3(kGroupThreads), 0, stream, masks, counts, max_count, nq,
+                     nwords, gh, plan_rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, gh, plan_rows, plan,
+                     plan_rows + (size_t)kPlanRows * groups);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes",
     "wise_dense_attn",

@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 6
+#define WISE_ABI_VERSION 7
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -118,8 +118,9 @@ size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
 /*
  * int32 entries of the optional execution plan wise_build_support can emit
  * beside the CSR schedule for bh rows of nq query blocks (0 on invalid sizes):
- * G + 1 + G*nq with G = bh * ceil(nq / 4) query-block groups (G entry
- * counts, the slot stride, and a fixed slot of nq entries per group).
+ * G + 1 + 4*G + G*nq with G = bh * (ceil(nq / 4) + ceil(nq / 16)) query-block
+ * groups (G entry counts, the slot stride, 4 row indices per group, and a fixed
+ * slot of nq entries per group).
  */
 size_t wise_build_support_plan_capacity(int bh, int nq);
 
@@ -146,17 +147,27 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 the same schedule (the execution metadata the WISE paper, App. B,
  *                 prepares with the sparse schedule), with
  *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq).
- *                 Query blocks are taken in groups of 4 consecutive blocks of one
- *                 (batch, head); group g = bh_index*ceil(nq/4) + q/4.  plan[g]
- *                 (g < G) is group g's entry count n_g, plan[G] = nq the slot
- *                 stride, and group g's entries are plan[G + 1 + g*nq ..
- *                 G + g*nq + n_g] (a fixed slot, so a reader loads the count and
- *                 the first entries at once); each entry is
- *                 (key block << 8) | membership, bit w of the membership set iff
- *                 query block 4*(g mod ceil(nq/4)) + w lists that key block.  Each
- *                 key block of the group's union appears once, in runs of 4 (the
- *                 tiles the kernel holds at once) that spread the member rows'
- *                 blocks evenly.
+ *                 The query blocks of each (batch, head) are dealt to
+ *                 GH = ceil(nq/4) + ceil(nq/16) groups of at most 4 blocks;
+ *                 group g = bh_index*GH + j, j = 0 .. GH-1.  A head's blocks are
+ *                 taken in order of scheduled block count, longest first (ties:
+ *                 lower index first), and packed 4 to a group, except that a
+ *                 group is closed early when its next block would raise its
+ *                 estimated run time (9 per started run of 4 union blocks plus 4
+ *                 per block of its longest row) above 5/4 of that of the
+ *                 schedule's longest row alone, as long as the blocks left fit in
+ *                 the groups left; groups are numbered in the order they are
+ *                 closed, and those left over list no blocks.  plan[g] (g < G) is
+ *                 group g's entry count n_g, plan[G] = nq the slot stride,
+ *                 plan[G + 1 + 4*g + w] (w < 4) the group's query block w or -1
+ *                 (its blocks first), and group g's entries are
+ *                 plan[5*G + 1 + g*nq .. 5*G + g*nq + n_g] (a fixed slot, so a
+ *                 reader loads the count and the first entries at once); each
+ *                 entry is (key block << 8) | membership, bit w of the
+ *                 membership set iff the group's query block w lists that key
+ *                 block.  Each key block of the group's union appears once, in
+ *                 runs of 4 (the tiles the kernel holds at once) that spread
+ *                 the member rows' blocks evenly.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.

@@ -68,7 +68,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 6
+    assert lib.wise_abi_version() == 7
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -127,10 +127,11 @@ def test_workspace_bytes(lib):
     f = lib.wise_build_support_workspace_bytes
     assert f(0, 8, 4) == 0 and f(1, 0, 4) == 0 and f(1, 8, 0) == 0 and f(1, 8, 65) == 0
     assert f(1, 4097, 4) == 0
-    # bitmask words per row and one count per row, 256-byte aligned sections
+    # bitmask words per row, one count per row and the largest count, 256-byte
+    # aligned sections
     def expect(bh, nq):
         al = lambda x: (x + 255) // 256 * 256
-        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4)
+        return al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4) + al(4)
     for bh, nq in ((1, 8), (32, 128), (32, 512), (3, 33)):
         assert f(bh, nq, 4) == expect(bh, nq)
 
@@ -138,10 +139,11 @@ def test_workspace_bytes(lib):
 def test_plan_capacity(lib):
     f = lib.wise_build_support_plan_capacity
     assert f(0, 8) == 0 and f(1, 0) == 0 and f(1, 4097) == 0
-    # group entry counts and the slot stride (G + 1) plus a fixed slot of nq entries per group
+    # group entry counts and the slot stride (G + 1), four row indices per group,
+    # and a fixed slot of nq entries per group
     for bh, nq in ((1, 8), (32, 128), (3, 33), (1, 1)):
-        g = bh * ((nq + 3) // 4)
-        assert f(bh, nq) == g + 1 + g * nq
+        g = bh * ((nq + 3) // 4 + (nq + 15) // 16)
+        assert f(bh, nq) == g + 1 + 4 * g + g * nq
 
 
 def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0, ws=P2,
@@ -190,8 +192,8 @@ def test_sparse_validation(lib):
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
     assert sp(d=80) == UNSUPPORTED
-    need = lib.wise_build_support_plan_capacity(1, 4)    # 1 group: counts, stride, 4 entry slots
-    assert need == 1 + 1 + 4
+    need = lib.wise_build_support_plan_capacity(1, 4)    # 2 groups: counts, stride, rows, 4 entry slots each
+    assert need == 2 + 1 + 2 * 4 + 2 * 4
     assert sp(plan=P, pcap=need - 1) == INVALID         # a group slot would be out of reach
     assert sp(plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
 
@@ -228,7 +230,7 @@ def test_blocked_builder_validation(lib):
     for bh, nq, steps, blk in ((2, 8, 4, 64), (3, 32, 4, 128), (1, 128, 1, 64)):
         fct = blk // 32
         nqb = nq // fct
-        base = al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4)
+        base = al(bh * nq * ((nq + 31) // 32) * 4) + al(bh * nq * 4) + al(4)
         extra = al(steps * bh * nqb * nqb * 4) + al(bh * nqb * ((nqb + 31) // 32) * 4) + al(bh * nqb * 4)
         assert f(bh, nq, steps, blk) == base + extra
     assert f(2, 8, 4, 32) == lib.wise_build_support_workspace_bytes(2, 8, 4)

@@ -326,22 +326,59 @@ def test_uniform_attention_closed_form_on_gpu():
 
 
 def _decode_plan(plan, bh, nq, rows_per_group=4):
-    """plan (host int32) -> {group: [(block, membership), ...]} in plan order: entry
-    counts plan[0..G), the slot stride plan[G] = nq, group g's entries in its slot
-    plan[G + 1 + g nq ..]."""
-    ng = (nq + rows_per_group - 1) // rows_per_group
-    groups = bh * ng
+    """plan (host int32) -> {group: (rows, [(block, membership), ...])} in plan order:
+    entry counts plan[0..G), the slot stride plan[G] = nq, four row indices per
+    group from plan[G + 1], group g's entries in its slot plan[5 G + 1 + g nq ..],
+    with G = bh (ceil(nq / 4) + ceil(nq / 16))."""
+    gh = (nq + rows_per_group - 1) // rows_per_group + (nq + 15) // 16
+    groups = bh * gh
     cnt = plan[:groups]
     assert int(plan[groups]) == nq and np.all(cnt >= 0) and np.all(cnt <= nq)
-    ent = plan[groups + 1:]
-    return {g: [(int(e) >> 8, int(e) & 255) for e in ent[g * nq:g * nq + cnt[g]]] for g in range(groups)}
+    rows = plan[groups + 1:groups + 1 + rows_per_group * groups].reshape(groups, rows_per_group)
+    ent = plan[groups + 1 + rows_per_group * groups:]
+    out = {}
+    for g in range(groups):
+        r = [int(x) for x in rows[g]]
+        valid = [x for x in r if x >= 0]
+        assert r == valid + [-1] * (rows_per_group - len(valid)), f"group {g} rows {r}"
+        out[g] = (valid, [(int(e) >> 8, int(e) & 255) for e in ent[g * nq:g * nq + cnt[g]]])
+    return out, gh
 
 
-@pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0)])
+def _expected_groups(rows_h, nq, gh, max_count):
+    """The grouping rule of wise_build_support's plan, on the host: a head's rows
+    longest first (ties: lower index first), packed up to 4 to a group, a group
+    closed early when the next row would raise its cost 9 ceil(u / 4) + 4 m (u
+    union blocks, m longest row) above 5/4 of the cost of the longest row alone,
+    while the rows left still fit in the groups left."""
+    cost = lambda u, m: 9 * ((u + 3) // 4) + 4 * m
+    cap = cost(max_count, max_count) * 5 // 4
+    order = sorted(range(nq), key=lambda q: (-len(rows_h[q]), q))
+    groups, cur, uni, tot, mx = [], [], set(), 0, 0
+    for k, q in enumerate(order):
+        c = len(rows_h[q])
+        close = len(cur) == 4
+        if (not close and cur and cost(tot + c, max(mx, c)) > cap
+                and len(groups) + 1 + (nq - k + 3) // 4 <= gh):
+            close = cost(len(uni | rows_h[q]), max(mx, c)) > cap
+        if close:
+            groups.append(cur)
+            cur, uni, tot, mx = [], set(), 0, 0
+        cur.append(q)
+        uni |= rows_h[q]
+        tot += c
+        mx = max(mx, c)
+    groups.append(cur)
+    return groups
+
+
+@pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0), (1, 300, 0.99)])
 def test_execution_plan_lists_each_union_block_once(bh, nq, eta):
-    """The plan of each 4-block group holds exactly the union of its rows' key blocks,
-    each once, with the membership bits of the oracle's supports; the sparse kernel
-    gives the same rows through the plan as through the CSR."""
+    """The plan deals each head's query blocks to groups of at most 4, every block
+    once, in order of scheduled block count (longest first, lower index first);
+    each group lists exactly the union of its rows' key blocks, each once, with the
+    membership bits of the oracle's supports; the sparse kernel gives the same rows
+    through the plan as through the CSR."""
     wise = _wise()
     rng = np.random.default_rng(bh * 1000 + nq)
     m = np.zeros((4, bh, nq, nq), dtype=np.float32)
@@ -363,19 +400,35 @@ def test_execution_plan_lists_each_union_block_once(bh, nq, eta):
             flags.append(fl)
     bad, _ = compare_supports(gpu_rows, ref_rows, flags)
     assert not bad
-    groups = _decode_plan(plan, bh, nq)
-    ng = (nq + 3) // 4
-    for g, ents in groups.items():
-        r0 = (g // ng) * nq + 4 * (g % ng)
-        rows = range(r0, min(r0 + 4, (g // ng + 1) * nq))
+    groups, gh = _decode_plan(plan, bh, nq)
+    max_count = max(len(r) for r in gpu_rows)
+    for h in range(bh):
+        rows_h = [set(gpu_rows[h * nq + q].tolist()) for q in range(nq)]
+        want_groups = _expected_groups(rows_h, nq, gh, max_count)
+        got_groups = [groups[h * gh + j][0] for j in range(gh) if groups[h * gh + j][0]]
+        assert got_groups == want_groups, f"head {h}: groups {got_groups} != {want_groups}"
+        dealt = [q for j in range(gh) for q in groups[h * gh + j][0]]
+        assert sorted(dealt) == list(range(nq)), f"head {h}: rows dealt {dealt}"
+        counts = [len(gpu_rows[h * nq + q]) for q in dealt]
+        assert [(-c, q) for c, q in zip(counts, dealt)] == sorted((-c, q) for c, q in zip(counts, dealt)), \
+            f"head {h}: rows not in count order"
+        seen_empty = False
+        for j in range(gh):
+            if not groups[h * gh + j][0]:
+                seen_empty = True
+            else:
+                assert not seen_empty, f"head {h}: a group after an empty one"
+    for g, (rows_g, ents) in groups.items():
+        h = g // gh
         blocks = [b for b, _ in ents]
         assert len(blocks) == len(set(blocks)), f"group {g} lists a block twice"
         want = {}
-        for w_, r in enumerate(rows):
-            for b in gpu_rows[r].tolist():
+        for w_, q in enumerate(rows_g):
+            for b in gpu_rows[h * nq + q].tolist():
                 want[b] = want.get(b, 0) | (1 << w_)
         assert dict(ents) == want, f"group {g}"
-        for w_, r in enumerate(rows):
+        for w_, q in enumerate(rows_g):
+            r = h * nq + q
             if set(gpu_rows[r].tolist()) == set(ref_rows[r].tolist()):
                 assert {b for b, mm in ents if (mm >> w_) & 1} == set(ref_rows[r].tolist())
     # sparse attention through the plan vs through the CSR rows vs the oracle
