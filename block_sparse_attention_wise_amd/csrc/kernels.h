@@ -74,12 +74,13 @@ size_t plan_capacity(int bh, int nq);
 // 2 MassMatched against the reference schedule (steps == 1)
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
                           const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream);
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, int plan_head_dim, void* workspace,
+                          hipStream_t stream);
 // selection at block size 32 f (f = 2 or 4) on 32-token masses; the CSR and plan
 // stay at 32-token granularity
 size_t support_blocked_workspace_bytes(int bh, int nq, int steps, int f);
 hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, double eta, int f, int32_t* row_ptr,
-                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace,
+                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, int plan_head_dim, void* workspace,
                                   hipStream_t stream);
 hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t* row_ptr, const int32_t* col_idx,
                                 int64_t cap, float* retained, hipStream_t stream);

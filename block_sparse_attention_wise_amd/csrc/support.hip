@@ -340,17 +340,17 @@ constexpr int kMasks = 1 << kPlanRows;
 // similar length waste the least time at the trip barriers, so each head's rows
 // are taken longest first (ties: lower index first) and packed greedily, up to
 // kPlanRows per group.  A group is closed early when the next row would push its
-// cost above 5/4 of that of the longest row of the whole schedule on its own:
-// the kernel cannot end before that row's group does, and much longer groups
-// would only lengthen the tail (measured on the 4k, Huginn and Llama
-// geometries: caps of 1 and 0.9 split too many groups at head_dim 128, no cap
-// leaves the tail long at head_dim 64; 5/4 is best at 128 and 96, neutral at
-// 64).  A head has at most plan_groups_per_head(nq) groups: once
+// cost above a cap, a fraction of the cost of the longest row of the whole
+// schedule on its own: the kernel cannot end before that row's group does, and
+// much longer groups would only lengthen the tail.  Measured on the 4k, Huginn
+// and Llama geometries, 5/4 is best at head_dim 128 and 96 (lower caps split
+// too many groups), 9/10 at 64, where three workgroups share a CU and the
+// longest groups decide the kernel's end.  A head has at most
+// plan_groups_per_head(nq) groups: once
 // the rows left would not fit in the groups left, groups are only closed when
 // full.  Groups come out longest first, the order the sparse kernel launches
 // them in; unused groups list no rows (-1).
 constexpr int kTripCost = 9, kTileCost = 4;
-constexpr int kCapNum = 5, kCapDen = 4;
 constexpr int kGroupThreads = 256;
 constexpr int kGroupChunk = 64;  // rows whose bitmasks are staged in LDS at once
 static_assert(kMaxNq <= 4096 && kMaxNq / 32 <= 128, "sort key and two union words per lane");
@@ -372,7 +372,7 @@ __device__ __forceinline__ int wave_sum_dpp(int x) {
 
 __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_t* masks, const int32_t* counts,
                                                                    const int32_t* max_count, int nq, int nwords,
-                                                                   int gh, int32_t* rows) {
+                                                                   int gh, int cap_num, int cap_den, int32_t* rows) {
   __shared__ uint32_t keys[kMaxNq];
   __shared__ uint32_t stage[kGroupChunk * (kMaxNq / 32)];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_
       __syncthreads();
     }
   const int mc = min(max(*max_count, 0), nq);
-  const int cap = group_cost(mc, mc) * kCapNum / kCapDen;
+  const int cap = group_cost(mc, mc) * cap_num / cap_den;
   int32_t* out = rows + (size_t)h * gh * kPlanRows;
   // wavefront 0 packs the rows in order: the open group's union bitmask (words
   // lane and lane + 64), the sum of its rows' counts (a bound on the union), its
@@ -637,7 +637,7 @@ hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t
 // CSR (row_ptr, col_idx, nnz) and, if plan != null, the execution plan from the
 // per-row bitmasks and counts in the workspace
 static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz, int32_t* plan,
-                                  void* workspace, hipStream_t stream) {
+                                  int plan_head_dim, void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -657,8 +657,12 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   const int gh = plan_groups_per_head(nq);
   const int groups = bh * gh;
   int32_t* plan_rows = plan + groups + 1;
+  // group cap relative to the longest row's cost: 9/10 for the head_dim 64
+  // kernel (three workgroups per CU, more slots than groups, so the longest
+  // groups decide its end), 5/4 for the others
+  const int cap_num = plan_head_dim == 64 ? 9 : 5, cap_den = plan_head_dim == 64 ? 10 : 4;
   hipLaunchKernelGGL(group_rows_kernel, dim3(bh), dim3(kGroupThreads), 0, stream, masks, counts, max_count, nq,
-                     nwords, gh, plan_rows);
+                     nwords, gh, cap_num, cap_den, plan_rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, gh, plan_rows, plan,
@@ -668,7 +672,8 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
 
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
                           const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream) {
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, int plan_head_dim, void* workspace,
+                          hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -688,7 +693,7 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, plan_head_dim, workspace, stream);
 }
 
 // ---------------------------------------------------------------- coarser blocks
@@ -748,7 +753,7 @@ size_t support_blocked_workspace_bytes(int bh, int nq, int steps, int f) {
 }
 
 hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, double eta, int f, int32_t* row_ptr,
-                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace,
+                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, int plan_head_dim, void* workspace,
                                   hipStream_t stream) {
   const int nqb = nq / f;
   const int nwb = (nqb + 31) / 32;
@@ -786,7 +791,7 @@ hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, 
                      masks, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, plan_head_dim, workspace, stream);
 }
 
 }  // namespace wise

@@ -67,8 +67,8 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seql
 // checks shared by the schedule builders
 // workspace_need: bytes of workspace the builder needs (0: the plain builder's)
 wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_t* row_ptr, int32_t* col_idx,
-                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity, void* workspace,
-                        size_t workspace_bytes, size_t workspace_need = 0) {
+                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
+                        int plan_head_dim, void* workspace, size_t workspace_bytes, size_t workspace_need = 0) {
   if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
   if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
   if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
@@ -80,6 +80,8 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
   if (plan != nullptr) {
     const size_t need = wise_build_support_plan_capacity(bh, nq);
     if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
+    if (plan_head_dim != 0 && plan_head_dim != 64 && plan_head_dim != 96 && plan_head_dim != 128)
+      return WISE_ERR_INVALID_ARG;
   }
   return WISE_OK;
 }
@@ -154,13 +156,14 @@ size_t wise_build_support_plan_capacity(int bh, int nq) {
 
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta, int32_t* row_ptr,
                                int32_t* col_idx, int64_t col_capacity, int32_t* nnz, int32_t* plan,
-                               int64_t plan_capacity, void* workspace, size_t workspace_bytes, void* stream) {
+                               int64_t plan_capacity, int plan_head_dim, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   wise_status st = check_build(bh, nq, num_steps, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
-                               workspace, workspace_bytes);
+                               plan_head_dim, workspace, workspace_bytes);
   if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, 0, nullptr, nullptr, 0, row_ptr, col_idx, nnz,
-                                plan, workspace, static_cast<hipStream_t>(stream));
+                                plan, plan_head_dim, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -175,22 +178,22 @@ size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps,
 
 wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps, const float* mass, float eta,
                                        int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
-                                       int32_t* plan, int64_t plan_capacity, void* workspace, size_t workspace_bytes,
-                                       void* stream) {
+                                       int32_t* plan, int64_t plan_capacity, int plan_head_dim, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   if (block == kBlock)
     return wise_build_support(bh, nq, num_steps, mass, eta, row_ptr, col_idx, col_capacity, nnz, plan,
-                              plan_capacity, workspace, workspace_bytes, stream);
+                              plan_capacity, plan_head_dim, workspace, workspace_bytes, stream);
   if (block != 2 * kBlock && block != 4 * kBlock) return WISE_ERR_UNSUPPORTED;
   const int f = block / kBlock;
   if (nq <= 0 || nq % f != 0) return WISE_ERR_INVALID_ARG;
   const size_t need = wise_build_support_blocked_workspace_bytes(bh, nq, num_steps, block);
   if (need == 0) return WISE_ERR_INVALID_ARG;
   wise_status st = check_build(bh, nq, num_steps, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
-                               workspace, workspace_bytes, need);
+                               plan_head_dim, workspace, workspace_bytes, need);
   if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support_blocked(mass, bh, nq, num_steps, (double)eta, f, row_ptr, col_idx, nnz, plan,
-                                        workspace, static_cast<hipStream_t>(stream));
+                                        plan_head_dim, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -198,9 +201,9 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
                                        const int32_t* ref_row_ptr, const int32_t* ref_col_idx,
                                        int64_t ref_col_capacity, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
-  wise_status st = check_build(bh, nq, 1, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity, workspace,
-                               workspace_bytes);
+                                       int plan_head_dim, void* workspace, size_t workspace_bytes, void* stream) {
+  wise_status st = check_build(bh, nq, 1, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
+                               plan_head_dim, workspace, workspace_bytes);
   if (st != WISE_OK) return st;
   int k;
   switch (kind) {
@@ -222,7 +225,7 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
     if (!aligned4(ref_row_ptr) || !aligned4(ref_col_idx)) return WISE_ERR_INVALID_ARG;
   }
   hipError_t e = launch_support(mass, bh, nq, 1, (double)eta, k, ref_row_ptr, ref_col_idx, ref_col_capacity, row_ptr,
-                                col_idx, nnz, plan, workspace, static_cast<hipStream_t>(stream));
+                                col_idx, nnz, plan, plan_head_dim, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 

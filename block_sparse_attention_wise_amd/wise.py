@@ -19,7 +19,7 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes",
     "wise_dense_attn",
@@ -51,15 +51,16 @@ def _load():
     lib.wise_build_support.restype = i32
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
-    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp, ctypes.c_size_t,
+                                       vp]
     lib.wise_build_support_blocked_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_blocked_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wise_build_support_blocked.restype = i32
-    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp,
+    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp,
                                                ctypes.c_size_t, vp]
     lib.wise_build_support_variant.restype = i32
-    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
-                                               ctypes.c_size_t, vp]
+    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, i32,
+                                               vp, ctypes.c_size_t, vp]
     lib.wise_retained_mass.restype = i32
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_sparse_attn.restype = i32
@@ -236,10 +237,11 @@ def _plan_args(schedule: Schedule):
 
 
 def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspace=None, stream=None,
-                  with_plan: bool = True, block: int = BLOCK):
+                  with_plan: bool = True, block: int = BLOCK, plan_head_dim: int = 0):
     """Selection + temporal union + CSR (+ execution plan) from 32-token masses
     [num_steps, b*h, nq, nq] (fp32).  block = 64 or 128 selects at that block size
-    (the schedule stays at 32-token granularity)."""
+    (the schedule stays at 32-token granularity); plan_head_dim is the head
+    dimension of the sparse attention that will use the plan (0: not known)."""
     if mass.dim() != 4 or mass.shape[2] != mass.shape[3]:
         raise ValueError("mass must be [num_steps, batch*heads, nq, nq]")
     if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
@@ -254,7 +256,8 @@ def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspa
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=mass.device)
     st = lib.wise_build_support_blocked(block, bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
                                         _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
-                                        *_plan_args(schedule), _ptr(workspace), workspace.numel(), _stream(stream))
+                                        *_plan_args(schedule), int(plan_head_dim), _ptr(workspace), workspace.numel(),
+                                        _stream(stream))
     _check(st, "wise_build_support_blocked" if block != BLOCK else "wise_build_support")
     return schedule
 
@@ -264,7 +267,8 @@ _VARIANTS = {"static": SUPPORT_STATIC, "size_matched": SUPPORT_SIZE_MATCHED, "ma
 
 
 def build_support_variant(kind, mass, *, eta: float = 0.95, reference: Schedule | None = None,
-                          schedule: Schedule | None = None, workspace=None, stream=None, with_plan: bool = True):
+                          schedule: Schedule | None = None, workspace=None, stream=None, with_plan: bool = True,
+                          plan_head_dim: int = 0):
     """Intervention-control schedule from one step's masses [b*h, nq, nq] (fp32):
     kind "static" (cumulative-eta support), "size_matched" or "mass_matched" (against
     the reference schedule)."""
@@ -288,8 +292,8 @@ def build_support_variant(kind, mass, *, eta: float = 0.95, reference: Schedule 
     ref_cap = reference.col_idx.numel() if reference is not None else 0
     st = lib.wise_build_support_variant(code, bh, nq, _ptr(mass), float(eta), ref_rp, ref_ci, ref_cap,
                                         _ptr(schedule.row_ptr), _ptr(schedule.col_idx), schedule.col_idx.numel(),
-                                        _ptr(schedule.nnz), *_plan_args(schedule), _ptr(workspace),
-                                        workspace.numel(), _stream(stream))
+                                        _ptr(schedule.nnz), *_plan_args(schedule), int(plan_head_dim),
+                                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "wise_build_support_variant")
     return schedule
 

@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 7
+#define WISE_ABI_VERSION 8
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -154,8 +154,8 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 lower index first), and packed 4 to a group, except that a
  *                 group is closed early when its next block would raise its
  *                 estimated run time (9 per started run of 4 union blocks plus 4
- *                 per block of its longest row) above 5/4 of that of the
- *                 schedule's longest row alone, as long as the blocks left fit in
+ *                 per block of its longest row) above a cap, as long as the
+ *                 blocks left fit in
  *                 the groups left; groups are numbered in the order they are
  *                 closed, and those left over list no blocks.  plan[g] (g < G) is
  *                 group g's entry count n_g, plan[G] = nq the slot stride,
@@ -168,6 +168,13 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 block.  Each key block of the group's union appears once, in
  *                 runs of 4 (the tiles the kernel holds at once) that spread
  *                 the member rows' blocks evenly.
+ *   plan_head_dim: the head dimension of the bf16 sparse attention that will
+ *                 walk the plan (64, 96 or 128), or 0 if not known; it sets the
+ *                 group cap: 9/10 of the longest row's cost at 64 (three
+ *                 workgroups per CU there, so the longest groups decide the
+ *                 kernel's end), 5/4 otherwise.  Any value gives a valid plan
+ *                 for every head dimension; others than these four are
+ *                 rejected when plan is not NULL, ignored when it is.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.
@@ -175,7 +182,7 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  */
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta,
                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                               int32_t* nnz, int32_t* plan, int64_t plan_capacity,
+                               int32_t* nnz, int32_t* plan, int64_t plan_capacity, int plan_head_dim,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -198,8 +205,8 @@ size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps,
 wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps, const float* mass,
                                        float eta, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int32_t* nnz, int32_t* plan,
-                                       int64_t plan_capacity, void* workspace, size_t workspace_bytes,
-                                       void* stream);
+                                       int64_t plan_capacity, int plan_head_dim, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * Intervention-control schedules of the WISE paper (App. B, intervention
@@ -233,7 +240,7 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
                                        const int32_t* ref_row_ptr, const int32_t* ref_col_idx,
                                        int64_t ref_col_capacity, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
-                                       void* workspace, size_t workspace_bytes, void* stream);
+                                       int plan_head_dim, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Retained attention mass of a schedule (the WISE paper, App. B: the fraction of

@@ -40,13 +40,14 @@ def lib():
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
-    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
-    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
-                                               ctypes.c_size_t, vp]
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp, ctypes.c_size_t,
+                                       vp]
+    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, i32,
+                                               vp, ctypes.c_size_t, vp]
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_build_support_blocked_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_blocked_workspace_bytes.argtypes = [i32, i32, i32, i32]
-    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp,
+    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp,
                                                ctypes.c_size_t, vp]
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
                                      f32, vp]
@@ -68,7 +69,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 7
+    assert lib.wise_abi_version() == 8
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -146,11 +147,11 @@ def test_plan_capacity(lib):
         assert f(bh, nq) == g + 1 + 4 * g + g * nq
 
 
-def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0, ws=P2,
-           wsb=None):
+def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0, hd=0,
+           ws=P2, wsb=None):
     cap = bh * nq * (nq + 1) // 2 if cap is None else cap
     wsb = lib.wise_build_support_workspace_bytes(bh, nq, steps) if wsb is None else wsb
-    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, plan, pcap, ws, wsb, None)
+    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, plan, pcap, hd, ws, wsb, None)
 
 
 def test_build_support_validation(lib):
@@ -167,6 +168,8 @@ def test_build_support_validation(lib):
     need = lib.wise_build_support_plan_capacity(2, 8)
     assert _build(lib, plan=P, pcap=need - 1) == INVALID
     assert _build(lib, plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
+    for hd in (-1, 1, 32, 80, 256):                      # plan head dimension: 0, 64, 96 or 128
+        assert _build(lib, plan=P, pcap=need, hd=hd) == INVALID, hd
     # a worst case beyond int32 row offsets is rejected
     assert _build(lib, bh=1 << 20, nq=4096, cap=1 << 62, wsb=1 << 62) == INVALID
 
@@ -204,7 +207,7 @@ def test_variant_and_retained_validation(lib):
     wsb = lib.wise_build_support_workspace_bytes(bh, nq, 1)
 
     def var(kind=1, mass=P, eta=0.95, rrp=P, rci=P, rcap=10, rp=P, ci=P, c=cap, nnz=P, ws=P2, w=wsb):
-        return lib.wise_build_support_variant(kind, bh, nq, mass, eta, rrp, rci, rcap, rp, ci, c, nnz, NULL, 0,
+        return lib.wise_build_support_variant(kind, bh, nq, mass, eta, rrp, rci, rcap, rp, ci, c, nnz, NULL, 0, 0,
                                               ws, w, None)
     assert var(kind=3) == INVALID and var(kind=-1) == INVALID
     assert var(kind=0, eta=0.0) == INVALID and var(kind=0, eta=1.5) == INVALID
@@ -239,7 +242,7 @@ def test_blocked_builder_validation(lib):
     def blk(block=64, bh=2, nq=8, steps=4, eta=0.95, cap=None, ws=P2, wsb=None):
         cap = bh * nq * (nq + 1) // 2 if cap is None else cap
         wsb = (f(bh, nq, steps, block) or 1 << 20) if wsb is None else wsb
-        return lib.wise_build_support_blocked(block, bh, nq, steps, P, eta, P, P, cap, P, NULL, 0, ws, wsb, None)
+        return lib.wise_build_support_blocked(block, bh, nq, steps, P, eta, P, P, cap, P, NULL, 0, 0, ws, wsb, None)
     assert blk(block=48) == UNSUPPORTED and blk(block=16) == UNSUPPORTED
     assert blk(nq=9) == INVALID                 # not a whole number of 64-token blocks
     assert blk(wsb=f(2, 8, 4, 64) - 1) == INVALID

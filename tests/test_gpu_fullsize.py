@@ -57,7 +57,7 @@ def test_fullsize_schedule_and_sparse_attention(name):
     (q13, k13, v13), dev13 = step_pair(g, 13)
     for eta in w.etas:
         note(f"{name} build eta={eta}")
-        sched = wise.build_support(mass, eta)
+        sched = wise.build_support(mass, eta, plan_head_dim=w.head_dim)
         note(f"{name} sparse eta={eta}")
         o, lse = wise.sparse_attn(*dev13, sched, want_lse=True)
         torch.cuda.synchronize()

@@ -345,14 +345,15 @@ def _decode_plan(plan, bh, nq, rows_per_group=4):
     return out, gh
 
 
-def _expected_groups(rows_h, nq, gh, max_count):
+def _expected_groups(rows_h, nq, gh, max_count, head_dim=0):
     """The grouping rule of wise_build_support's plan, on the host: a head's rows
     longest first (ties: lower index first), packed up to 4 to a group, a group
     closed early when the next row would raise its cost 9 ceil(u / 4) + 4 m (u
-    union blocks, m longest row) above 5/4 of the cost of the longest row alone,
-    while the rows left still fit in the groups left."""
+    union blocks, m longest row) above 5/4 (9/10 for head_dim 64) of the cost of
+    the longest row alone, while the rows left still fit in the groups left."""
     cost = lambda u, m: 9 * ((u + 3) // 4) + 4 * m
-    cap = cost(max_count, max_count) * 5 // 4
+    num, den = (9, 10) if head_dim == 64 else (5, 4)
+    cap = cost(max_count, max_count) * num // den
     order = sorted(range(nq), key=lambda q: (-len(rows_h[q]), q))
     groups, cur, uni, tot, mx = [], [], set(), 0, 0
     for k, q in enumerate(order):
@@ -372,8 +373,9 @@ def _expected_groups(rows_h, nq, gh, max_count):
     return groups
 
 
-@pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0), (1, 300, 0.99)])
-def test_execution_plan_lists_each_union_block_once(bh, nq, eta):
+@pytest.mark.parametrize("bh,nq,eta,hd", [(3, 37, 0.9, 0), (2, 8, 0.5, 128), (1, 130, 0.95, 64), (2, 5, 1.0, 96),
+                                          (1, 300, 0.99, 0), (2, 64, 0.9, 64)])
+def test_execution_plan_lists_each_union_block_once(bh, nq, eta, hd):
     """The plan deals each head's query blocks to groups of at most 4, every block
     once, in order of scheduled block count (longest first, lower index first);
     each group lists exactly the union of its rows' key blocks, each once, with the
@@ -386,8 +388,8 @@ def test_execution_plan_lists_each_union_block_once(bh, nq, eta):
         for r in range(bh):
             for qb in range(nq):
                 m[s, r, qb, :qb + 1] = rng.dirichlet(np.full(qb + 1, 0.4))
-    note(f"plan bh={bh} nq={nq} eta={eta}")
-    sched = wise.build_support(torch.from_numpy(m).to(DEV), eta)
+    note(f"plan bh={bh} nq={nq} eta={eta} plan_head_dim={hd}")
+    sched = wise.build_support(torch.from_numpy(m).to(DEV), eta, plan_head_dim=hd)
     torch.cuda.synchronize()
     assert sched.plan is not None
     plan = sched.plan.cpu().numpy()
@@ -404,7 +406,7 @@ def test_execution_plan_lists_each_union_block_once(bh, nq, eta):
     max_count = max(len(r) for r in gpu_rows)
     for h in range(bh):
         rows_h = [set(gpu_rows[h * nq + q].tolist()) for q in range(nq)]
-        want_groups = _expected_groups(rows_h, nq, gh, max_count)
+        want_groups = _expected_groups(rows_h, nq, gh, max_count, hd)
         got_groups = [groups[h * gh + j][0] for j in range(gh) if groups[h * gh + j][0]]
         assert got_groups == want_groups, f"head {h}: groups {got_groups} != {want_groups}"
         dealt = [q for j in range(gh) for q in groups[h * gh + j][0]]
