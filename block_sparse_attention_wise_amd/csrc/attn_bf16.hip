@@ -414,22 +414,31 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   const int i = lane & 31, h = lane >> 5;
   const int ngroups = (a.nq + W - 1) / W;
   const int bhn = a.rows / a.nq;
-  // Longest-first order over all heads: workgroup p takes the (p / bhn)-th longest
-  // query group of head slot s = p % bhn.  Consecutive workgroups land on
-  // different XCDs (XCD s mod 8 when bhn is a multiple of 8); slot s maps to head
-  // (s mod 8) * bhn/8 + s / 8, so each XCD works on one contiguous run of heads,
-  // and the query heads of one key-value group share that XCD's L2.
-  const int slot = blockIdx.x % bhn;
-  const int bh = (bhn & 7) == 0 ? (slot & 7) * (bhn >> 3) + (slot >> 3) : slot;
   constexpr bool PLAN_ROWS = SPARSE && !SUB;  // rows may come from an execution plan
   const bool use_plan = PLAN_ROWS && a.plan != nullptr;
+  const int per_head = use_plan ? plan_groups_per_head(a.nq) : ngroups;  // query groups per head
+  // Consecutive workgroups land on consecutive XCDs (p mod 8).  XCD x works on
+  // one contiguous run of heads, x * bhn/8 .. (x+1) * bhn/8 - 1 (the first bhn
+  // mod 8 runs one head longer), so the query heads of one key-value group share
+  // that XCD's L2; its k-th workgroup (k = p / 8) takes the (k / run)-th longest
+  // query group of head k mod run of its run: longest first over all heads.
+  // The grid has 8 * ceil(bhn / 8) * per_head workgroups; those past an XCD's
+  // run hold no work.
+  int bh, rank;
+  {
+    const int x = (int)(blockIdx.x & 7u), k = (int)(blockIdx.x >> 3);
+    const int base = bhn >> 3, rem = bhn & 7;
+    const int run = base + (x < rem ? 1 : 0), start = x * base + min(x, rem);
+    if (k >= run * per_head) return;  // uniform over the workgroup
+    bh = start + k % run;
+    rank = k / run;
+  }
   int qb, qlast, pgroup = 0;
   if (use_plan) {
-    // the plan's groups of this head come longest first: workgroup p takes the
-    // (p / bhn)-th; its rows are listed first, -1 after (rows outside 0..nq-1
-    // are ignored)
-    const int gh = plan_groups_per_head(a.nq);
-    pgroup = bh * gh + (int)(blockIdx.x / bhn);
+    // the plan's groups of this head come longest first; rank-th group; its
+    // rows are listed first, -1 after (rows outside 0..nq-1 are ignored)
+    const int gh = per_head;
+    pgroup = bh * gh + rank;
     const int32_t* gr = a.plan + bhn * gh + 1 + (size_t)kPlanRows * pgroup;
     qb = -1;
     qlast = -1;
@@ -442,7 +451,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     }
     if (qlast < 0) return;  // an empty group (uniform over the workgroup)
   } else {
-    const int grp = ngroups - 1 - (int)(blockIdx.x / bhn);
+    const int grp = ngroups - 1 - rank;
     qb = W * grp + wave;
     qlast = min(W * grp + W, a.nq) - 1;
   }
@@ -841,7 +850,7 @@ static void launch_mode(const AttnBf16Args& a, hipStream_t stream) {
   constexpr int w = stream_waves<D, MODE>();
   const int bhn = a.rows / a.nq;
   const int per_head = MODE == kSparse && a.plan != nullptr ? plan_groups_per_head(a.nq) : (a.nq + w - 1) / w;
-  const dim3 grid(bhn * per_head), block(64 * w);
+  const dim3 grid(8 * ((bhn + 7) / 8) * per_head), block(64 * w);  // XCD-aligned head runs
   if constexpr (MODE == kSparse || MODE == kSparse16)
     hipLaunchKernelGGL((attn_sparse_kernel<D, MODE>), grid, block, 0, stream, a);
   else
