@@ -208,7 +208,7 @@ def test_eta_one_sparse_equals_dense(name):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("batch,heads,kv,n", [(1, 1, 1, 32), (2, 3, 3, 96), (1, 2, 2, 160), (2, 4, 2, 96),
-                                               (1, 6, 1, 64)])
+                                               (1, 6, 1, 64), (1, 11, 11, 64), (2, 13, 1, 96)])
 def test_shapes_batch_and_head_dim(dtype, d, batch, heads, kv, n):
     wise = _wise()
     rng = np.random.default_rng(batch * 100 + heads * 10 + n + d)
@@ -374,7 +374,7 @@ def _expected_groups(rows_h, nq, gh, max_count, head_dim=0):
 
 
 @pytest.mark.parametrize("bh,nq,eta,hd", [(3, 37, 0.9, 0), (2, 8, 0.5, 128), (1, 130, 0.95, 64), (2, 5, 1.0, 96),
-                                          (1, 300, 0.99, 0), (2, 64, 0.9, 64)])
+                                          (1, 300, 0.99, 0), (2, 64, 0.9, 64), (11, 16, 0.9, 96)])
 def test_execution_plan_lists_each_union_block_once(bh, nq, eta, hd):
     """The plan deals each head's query blocks to groups of at most 4, every block
     once, in order of scheduled block count (longest first, lower index first);
