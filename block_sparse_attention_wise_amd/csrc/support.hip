@@ -353,6 +353,7 @@ constexpr int kMasks = 1 << kPlanRows;
 constexpr int kTripCost = 9, kTileCost = 4;
 constexpr int kGroupThreads = 256;
 constexpr int kGroupChunk = 64;  // rows whose bitmasks are staged in LDS at once
+constexpr int kRankSortMax = 1024;  // rows sorted by rank (else bitonic)
 static_assert(kMaxNq <= 4096 && kMaxNq / 32 <= 128, "sort key and two union words per lane");
 
 __device__ __forceinline__ int group_cost(int u, int m) {
@@ -377,7 +378,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_
   __shared__ uint32_t stage[kGroupChunk * (kMaxNq / 32)];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int32_t* cnt = counts + (size_t)h * nq;
-  // sort keys (count descending, row ascending), bitonic over a power of two
+  // sort keys (count descending, row ascending; all distinct): up to
+  // kRankSortMax rows each key goes to its rank, the number of smaller keys
+  // (broadcast LDS reads, no barrier per pass); beyond, bitonic over a power of two
   int n2 = 1;
   while (n2 < nq) n2 <<= 1;
   for (int q = tid; q < n2; q += kGroupThreads) {
@@ -385,6 +388,20 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_
     keys[q] = q < nq ? ((uint32_t)(kMaxNq - c) << 12) | (uint32_t)q : 0xFFFFFFFFu;
   }
   __syncthreads();
+  if (nq <= kRankSortMax) {
+    uint32_t* sorted = stage;  // free until the rows are packed
+    for (int q = tid; q < nq; q += kGroupThreads) {
+      const uint32_t kq = keys[q];
+      int rank = 0;
+#pragma unroll 8
+      for (int p = 0; p < nq; ++p) rank += keys[p] < kq ? 1 : 0;
+      sorted[rank] = kq;
+    }
+    __syncthreads();
+    for (int q = tid; q < nq; q += kGroupThreads) keys[q] = sorted[q];
+    __syncthreads();
+    n2 = 1;  // the bitonic passes below are skipped
+  }
   for (int k = 2; k <= n2; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < n2; i += kGroupThreads) {
