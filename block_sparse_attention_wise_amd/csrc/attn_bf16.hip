@@ -41,6 +41,47 @@ struct Tile {
   static constexpr int C8 = D / 8;         // 16-byte chunks per row
 };
 
+// One trip buffer of the direct-to-LDS copies: TRIP K tiles, then TRIP V tiles,
+// each in the padded row layout of Tile<D> (CK / CV 16-byte chunks per row) and
+// each rounded up to whole wave-copies: one buffer_load_dwordx4 ... lds writes
+// 64 consecutive 16-byte chunks, lane j the j-th, so chunk p of a tile region
+// holds row p / CK (or CV), column chunk p % CK of the tile.
+template <int D, int TRIP>
+struct DmaTrip {
+  using T = Tile<D>;
+  static constexpr int CK = T::KSTRIDE / 8, CV = T::VSTRIDE / 8;
+  static constexpr int KI = (32 * CK + 63) / 64, VI = (32 * CV + 63) / 64;  // wave-copies per tile
+  static constexpr int KB = 1024 * KI, VB = 1024 * VI;                      // bytes per tile region
+  static constexpr int NI = TRIP * (KI + VI);                               // wave-copies per trip
+  static constexpr int BYTES = TRIP * (KB + VB);
+};
+// The 32-key tiles a 16-token sparse row can reach (2 * nq <= 2048).
+constexpr int kSubTileWords = 32;
+
+// Raw buffer resource over `bytes` bytes at p (no stride, 32-bit data format;
+// reads past the end return 0), wave-uniform.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 buffer_resource(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  u32x4 r = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  r[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  r[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  return r;
+}
+// One wave-copy: lane j fetches 16 bytes at resource offset soff + voff and the
+// hardware writes them to LDS bytes [lds + 16 j, lds + 16 j + 16).  Written as
+// assembly so that the compiler, which cannot tell the two trip buffers apart,
+// inserts no waits for these copies before unrelated LDS reads; the streaming
+// loop waits for them itself (vmcnt(0) and a barrier at the end of each trip).
+// M0 is set here and not restored: nothing else in the attention kernels uses it.
+__device__ __forceinline__ void copy_to_lds(u32x4 rs, const void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(la), "v"(voff), "s"(rs),
+               "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "m0");
+}
+
 // Key index (within a 32-key block) held by accumulator register r of a lane in
 // half h of the 32x32 MFMA result.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -324,13 +365,13 @@ struct DenseList {
   __device__ __forceinline__ int next() { return b < nb ? (b++ << kEntryShift) | 0xFF : -1; }
 };
 // union of the workgroup's W rows, ascending, from their bitmasks in LDS
-template <int W>
+template <int W, int MW>
 struct UnionList {
-  const uint32_t* masks;  // [W][kMaxMaskWords] in LDS
+  const uint32_t* masks;  // [W][MW] in LDS
   int nwords, wd;
   uint32_t u;
   __device__ __forceinline__ uint32_t row_word(int r, int w) const {
-    return __builtin_amdgcn_readfirstlane(masks[r * kMaxMaskWords + w]);
+    return __builtin_amdgcn_readfirstlane(masks[r * MW + w]);
   }
   __device__ __forceinline__ uint32_t word_union(int w) const {
     uint32_t x = 0u;
@@ -394,18 +435,20 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // longer (fewer barriers, more loads in flight)
   constexpr int TRIP = SPARSE ? kSparseTrip : 2;
 
-  // the trip's K and V tiles; the block-mass sweep reuses the same LDS for
-  // MTRIP K-only tiles per trip
+  // Two trip buffers (the trip being computed, the next one being copied), each
+  // TRIP K tiles then TRIP V tiles in the padded row layouts of Tile<D>, filled
+  // by direct-to-LDS copies (DmaTrip).  Separate arrays, so the compiler can
+  // tell that reads of one buffer do not depend on the copies into the other.
+  // The block-mass sweep reuses buffer 0 for MTRIP K-only tiles per trip.
+  using DT = DmaTrip<D, TRIP>;
   constexpr int MTRIP = 4;
   typedef __bf16 KTile[32 * T::KSTRIDE];
-  typedef __bf16 VTile[32 * T::VSTRIDE];
-  constexpr size_t TILES_BYTES = TRIP * (sizeof(KTile) + sizeof(VTile));
-  constexpr size_t SWEEP_BYTES = MASS ? MTRIP * sizeof(KTile) : 0;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_tiles[TILES_BYTES > SWEEP_BYTES ? TILES_BYTES : SWEEP_BYTES];
-  KTile* const kt = reinterpret_cast<KTile*>(lds_tiles);
-  VTile* const vt = reinterpret_cast<VTile*>(lds_tiles + TRIP * sizeof(KTile));
-  KTile* const mk = reinterpret_cast<KTile*>(lds_tiles);
-  __shared__ uint32_t rmask[SPARSE ? W * kMaxMaskWords : 1];
+  static_assert(!MASS || MTRIP * sizeof(KTile) <= DT::BYTES, "sweep tiles fit buffer 0");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[DT::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[DT::BYTES];
+  KTile* const mk = reinterpret_cast<KTile*>(lds_b0);
+  constexpr int MW = SUB ? kSubTileWords : kMaxMaskWords;  // row bitmask words
+  __shared__ uint32_t rmask[SPARSE ? W * MW : 1];
   __shared__ uint32_t smask[SUB ? W * 2 * kSubWords : 1];  // the two 16-token rows of each wavefront
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -487,7 +530,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     // this wavefront's row as a bitmask over key blocks (entries outside 0..qb
     // and offsets outside 0..col_cap are ignored; duplicates count once)
     const int nwords = (qlast >> 5) + 1;
-    uint32_t* my = rmask + wave * kMaxMaskWords;
+    uint32_t* my = rmask + wave * MW;
     for (int w = lane; w < nwords; w += 64) my[w] = 0u;
     if (SUB)
       for (int w = lane; w < 2 * kSubWords; w += 64) smask[wave * 2 * kSubWords + w] = 0u;
@@ -526,29 +569,62 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     __syncthreads();
   }
 
-  // cooperative tile copy: chunk c = tid + NTHR*u -> row c / C8, column chunk c % C8
-  struct Stage {
-    bf16x8 k[CPT], v[CPT];
-  };
-  auto gload = [&](Stage& r, int e, bool with_v) {
-    const int b = e >> kEntryShift;
+  // Direct-to-LDS tile copies.  A trip buffer has 2 TRIP regions (the K and V
+  // tile of each of its tiles); with W >= 2 TRIP wavefronts, W / (2 TRIP) of
+  // them share a region, taking every (W / (2 TRIP))-th of its wave-copies;
+  // with fewer, each wavefront fills whole regions.  Which chunk of the source
+  // tile each lane fetches is fixed for the kernel; only the block numbers
+  // change per trip.
+  constexpr int NR = 2 * TRIP;                        // regions per trip buffer
+  constexpr int WPR = W >= NR ? W / NR : 1;           // wavefronts per region
+  constexpr int RPW = W >= NR ? 1 : NR / W;           // regions per wavefront
+  static_assert(W >= NR ? W % NR == 0 : NR % W == 0, "regions and wavefronts");
+  constexpr int XS = (DT::VI > DT::KI ? DT::VI : DT::KI);
+  constexpr int S = (XS + WPR - 1) / WPR;             // copies per region and wavefront, at most
+  const int sub = wave / NR;                          // W >= NR: this wavefront's share of its region
+  uint32_t voff[RPW][S];                              // lane's byte offset within the source tile
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NTHR * u;
-      if (CHUNKS % NTHR == 0 || c < CHUNKS) {
-        const size_t off = (size_t)(32 * b + c / T::C8) * D + (c % T::C8) * 8;
-        r.k[u] = *reinterpret_cast<const bf16x8*>(kh + off);
-        if (with_v) r.v[u] = *reinterpret_cast<const bf16x8*>(vh + off);
-      }
+  for (int k = 0; k < RPW; ++k) {
+    const int r = W >= NR ? wave % NR : wave + W * k;  // region: tile r % TRIP, V if r >= TRIP
+    const bool isv = r >= TRIP;
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      const int p = 64 * (sub + WPR * c) + lane;  // chunk of the padded tile region
+      const int row = isv ? p / DT::CV : p / DT::CK, ch = isv ? p % DT::CV : p % DT::CK;
+      // chunks past a row's data (padding) and past the tile re-read chunk 0
+      voff[k][c] = row < 32 && ch < T::C8 ? (uint32_t)(row * D + ch * 8) * 2u : 0u;
     }
-  };
-  auto lstore = [&](const Stage& r, int buf, bool with_v) {
+  }
+  // buffer resources over this head's K and V (out-of-range reads return 0)
+  const uint32_t kv_bytes = (uint32_t)a.seqlen * (uint32_t)(D * 2);
+  const u32x4 rsk = buffer_resource(kh, kv_bytes), rsv = buffer_resource(vh, kv_bytes);
+  auto issue = [&](unsigned char* buf, const int (&c)[TRIP]) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NTHR * u;
-      if (CHUNKS % NTHR == 0 || c < CHUNKS) {
-        *reinterpret_cast<bf16x8*>(&kt[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = r.k[u];
-        if (with_v) *reinterpret_cast<bf16x8*>(&vt[buf][(c / T::C8) * T::VSTRIDE + (c % T::C8) * 8]) = r.v[u];
+    for (int k = 0; k < RPW; ++k) {
+      const int r = W >= NR ? wave % NR : wave + W * k;
+      const bool isv = r >= TRIP;
+      const int u = isv ? r - TRIP : r;
+      int e = c[0];
+#pragma unroll
+      for (int t = 1; t < TRIP; ++t)
+        if (u == t) e = c[t];
+      if (e < 0) continue;
+      unsigned char* dst = buf + (isv ? TRIP * DT::KB + u * DT::VB : u * DT::KB);
+      const int soff = (e >> kEntryShift) * (32 * D * 2);
+      if (isv) {
+#pragma unroll
+        for (int cc = 0; cc < S; ++cc) {
+          const int x = sub + WPR * cc;
+          if (x < DT::VI)
+            copy_to_lds(rsv, dst + 1024 * x, voff[k][cc], soff);
+        }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < S; ++cc) {
+          const int x = sub + WPR * cc;
+          if (x < DT::KI)
+            copy_to_lds(rsk, dst + 1024 * x, voff[k][cc], soff);
+        }
       }
     }
   };
@@ -558,37 +634,36 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     return active && (!SPARSE || ((e >> wave) & 1)) && (e >> kEntryShift) <= qb;
   };
 
-  // Runs `work(entries)` over the list, TRIP blocks per trip: the trip's
-  // tiles sit in LDS buffers 0..TRIP-1 while the next trip's are fetched into
-  // the register stages; every load is waited for inside the trip it was issued
-  // in, so the compiler's wait counts stay exact across the loop back-edge.
-  auto stream = [&](auto& list, bool with_v, auto&& work) {
-    Stage r[TRIP];
-    int c[TRIP];
+  // Runs `work(buffer, entries)` over the list, TRIP blocks per trip, with two
+  // trip buffers: while one trip is computed, the next one's copies run into the
+  // other buffer.  One barrier per trip, after each wavefront has waited for its
+  // own copies: then the next trip's tiles are complete and every wavefront is
+  // done with the buffer the trip after it will overwrite.
+  auto fetch = [&](auto& list, int (&c)[TRIP], bool more) {
 #pragma unroll
-    for (int u = 0; u < TRIP; ++u) c[u] = (u == 0 || c[u - 1] >= 0) ? list.next() : -1;
-#pragma unroll
-    for (int u = 0; u < TRIP; ++u)
-      if (c[u] >= 0) gload(r[u], c[u], with_v);
-#pragma unroll
-    for (int u = 0; u < TRIP; ++u)
-      if (c[u] >= 0) lstore(r[u], u, with_v);
+    for (int u = 0; u < TRIP; ++u) {
+      c[u] = more ? list.next() : -1;
+      more = c[u] >= 0;
+    }
+  };
+  auto stream = [&](auto& list, auto&& work) {
+    int c0[TRIP], c1[TRIP];
+    fetch(list, c0, true);
+    issue(lds_b0, c0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    while (c[0] >= 0) {
-      int n[TRIP];
-#pragma unroll
-      for (int u = 0; u < TRIP; ++u) n[u] = (u == 0 ? c[TRIP - 1] >= 0 : n[u - 1] >= 0) ? list.next() : -1;
-#pragma unroll
-      for (int u = 0; u < TRIP; ++u)
-        if (n[u] >= 0) gload(r[u], n[u], with_v);
-      work(c);
+    while (c0[0] >= 0) {
+      fetch(list, c1, c0[TRIP - 1] >= 0);
+      issue(lds_b1, c1);
+      work(lds_b0, c0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-#pragma unroll
-      for (int u = 0; u < TRIP; ++u)
-        if (n[u] >= 0) lstore(r[u], u, with_v);
+      if (c1[0] < 0) break;
+      fetch(list, c0, c1[TRIP - 1] >= 0);
+      issue(lds_b0, c0);
+      work(lds_b1, c1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-#pragma unroll
-      for (int u = 0; u < TRIP; ++u) c[u] = n[u];
     }
   };
 
@@ -610,7 +685,10 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     return (int)((__builtin_amdgcn_readfirstlane(sm[0]) >> sh) & 3u) |
            (int)(((__builtin_amdgcn_readfirstlane(sm[kSubWords]) >> sh) & 3u) << 2);
   };
-  auto attend = [&](const int (&c)[TRIP]) {
+  auto attend = [&](const unsigned char* buf, const int (&c)[TRIP]) {
+    const __bf16* const kb = reinterpret_cast<const __bf16*>(buf);  // K tile u at kb + u * KE
+    const __bf16* const vb = reinterpret_cast<const __bf16*>(buf + TRIP * DT::KB);
+    constexpr int KE = DT::KB / 2, VE = DT::VB / 2;
     int mine = 0, dg = 0;
 #pragma unroll
     for (int u = 0; u < TRIP; ++u) {
@@ -622,8 +700,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       mine &= mine - 1;
       const int u1 = __builtin_ctz(mine);
       mine &= mine - 1;
-      const __bf16* const kp[2] = {kt[u0], kt[u1]};
-      const __bf16* const vp[2] = {vt[u0], vt[u1]};
+      const __bf16* const kp[2] = {kb + u0 * KE, kb + u1 * KE};
+      const __bf16* const vp[2] = {vb + u0 * VE, vb + u1 * VE};
       const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
       const int bi[2] = {c[u0] >> kEntryShift, c[u1] >> kEntryShift};
       attend_tiles<D, 2, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
@@ -632,8 +710,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     while (mine) {
       const int u0 = __builtin_ctz(mine);
       mine &= mine - 1;
-      const __bf16* const kp[1] = {kt[u0]};
-      const __bf16* const vp[1] = {vt[u0]};
+      const __bf16* const kp[1] = {kb + u0 * KE};
+      const __bf16* const vp[1] = {vb + u0 * VE};
       const bool dp[1] = {((dg >> u0) & 1) != 0};
       const int bi[1] = {c[u0] >> kEntryShift};
       attend_tiles<D, 1, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2, sub4(bi[0]) | 0xF0,
@@ -641,14 +719,14 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     }
   };
   if (use_plan) {
-    stream(plist, true, attend);
+    stream(plist, attend);
   } else if (SPARSE) {
-    UnionList<W> list{rmask, (qlast >> 5) + 1, 0, 0u};
+    UnionList<W, MW> list{rmask, (qlast >> 5) + 1, 0, 0u};
     list.u = list.word_union(0);
-    stream(list, true, attend);
+    stream(list, attend);
   } else {
     DenseList list{0, qlast + 1};
-    stream(list, true, attend);
+    stream(list, attend);
   }
 
   float lse2 = -INFINITY;

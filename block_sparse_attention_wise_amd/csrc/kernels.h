@@ -13,7 +13,7 @@ namespace wise {
 // may stay empty); without one, to ceil(nq / kPlanRows) groups of consecutive
 // rows.
 constexpr int kPlanRows = 4;
-constexpr int kPlanTrip = 4;
+constexpr int kPlanTrip = 2;
 __host__ __device__ constexpr int plan_groups_per_head(int nq) {
   return (nq + kPlanRows - 1) / kPlanRows + (nq + 15) / 16;
 }
