@@ -32,27 +32,38 @@ namespace wise {
 template <int D>
 struct Tile {
   static constexpr int NC = D / 16;        // 16-wide k chunks of Q K^T
-  static constexpr int HALF = D / 2;       // elements of a row owned by one lane half
   static constexpr int NT = D / 32;        // 32-wide column tiles of O
-  static constexpr int VSTRIDE = D == 96 ? D : D + 32;  // V tile row stride (elements); 2*VSTRIDE = 64 or 192 mod
-                                           // 256 bytes keeps the transposing reads conflict free
-  static constexpr int KSTRIDE = D + 8;    // K tile row stride (elements); 16-byte reads of 16
-                                           // consecutive rows hit distinct banks
   static constexpr int C8 = D / 8;         // 16-byte chunks per row
+  static constexpr int BYTES = 64 * D;     // one 32-row K or V tile in LDS
+  static constexpr int SKSTRIDE = D + 8;   // row stride (elements) of the block-mass sweep's K tiles;
+                                           // 16-byte reads of 16 consecutive rows hit distinct banks
 };
 
+// LDS layout of a K or V tile (32 rows of C8 16-byte chunks, no padding): 1 KiB
+// blocks of 16 rows x 4 chunks, block 2 (ch / 4) + r / 16; in a block row r % 16
+// takes 64 bytes, its 4 chunks XOR-permuted by (r / 4) % 4.  16 consecutive rows
+// of one chunk, and 4 consecutive rows of 4 chunks, then fill the 16 bank slots
+// of 16 bytes once each: the K fragment reads (16 rows of one chunk per 16
+// lanes) and the V transposing reads (4 rows x 32 bytes per 16 lanes) are
+// conflict free.  One direct-to-LDS copy (64 lanes x 16 bytes) fills one block
+// from 16 row segments of 64 bytes, permuted only within each 64-byte segment,
+// which the memory pipeline coalesces as well as a contiguous kilobyte.
+__host__ __device__ constexpr int tile_offset(int r, int ch) {
+  return 1024 * (2 * (ch >> 2) + (r >> 4)) + 64 * (r & 15) + 16 * ((ch & 3) ^ ((r >> 2) & 3));
+}
+
+// The contraction index of Q K^T: MFMA step c, lane half h takes d-chunk 2 c + h
+// (8 elements) in both operands.
+__host__ __device__ constexpr int qk_chunk(int c, int h) { return 2 * c + h; }
+
 // One trip buffer of the direct-to-LDS copies: TRIP K tiles, then TRIP V tiles,
-// each in the padded row layout of Tile<D> (CK / CV 16-byte chunks per row) and
-// each rounded up to whole wave-copies: one buffer_load_dwordx4 ... lds writes
-// 64 consecutive 16-byte chunks, lane j the j-th, so chunk p of a tile region
-// holds row p / CK (or CV), column chunk p % CK of the tile.
+// D / 16 wave-copies each.
 template <int D, int TRIP>
 struct DmaTrip {
   using T = Tile<D>;
-  static constexpr int CK = T::KSTRIDE / 8, CV = T::VSTRIDE / 8;
-  static constexpr int KI = (32 * CK + 63) / 64, VI = (32 * CV + 63) / 64;  // wave-copies per tile
-  static constexpr int KB = 1024 * KI, VB = 1024 * VI;                      // bytes per tile region
-  static constexpr int NI = TRIP * (KI + VI);                               // wave-copies per trip
+  static constexpr int CI = D / 16;                 // wave-copies per tile
+  static constexpr int KB = T::BYTES, VB = T::BYTES;  // bytes per tile region
+  static constexpr int NI = 2 * TRIP * CI;          // wave-copies per trip
   static constexpr int BYTES = TRIP * (KB + VB);
 };
 // The 32-key tiles a 16-token sparse row can reach (2 * nq <= 2048).
@@ -75,8 +86,11 @@ __device__ __forceinline__ u32x4 buffer_resource(const void* p, uint32_t bytes) 
 // inserts no waits for these copies before unrelated LDS reads; the streaming
 // loop waits for them itself (vmcnt(0) and a barrier at the end of each trip).
 // M0 is set here and not restored: nothing else in the attention kernels uses it.
-__device__ __forceinline__ void copy_to_lds(u32x4 rs, const void* lds, uint32_t voff, uint32_t soff) {
-  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const void*)lds);
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void copy_to_lds(u32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(la), "v"(voff), "s"(rs),
                "s"(__builtin_amdgcn_readfirstlane(soff))
                : "m0");
@@ -88,9 +102,9 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 
 template <int D>
 __device__ __forceinline__ void load_frag(bf16x8 (&f)[Tile<D>::NC], const __bf16* rowp, int h) {
-  const bf16x8* p = reinterpret_cast<const bf16x8*>(rowp + h * Tile<D>::HALF);
+  const bf16x8* p = reinterpret_cast<const bf16x8*>(rowp);
 #pragma unroll
-  for (int c = 0; c < Tile<D>::NC; ++c) f[c] = p[c];
+  for (int c = 0; c < Tile<D>::NC; ++c) f[c] = p[qk_chunk(c, h)];
 }
 
 // A operand (V^T rows dcol = 32*t + lane%32, k-slots = keys) for output tile t
@@ -98,20 +112,41 @@ __device__ __forceinline__ void load_frag(bf16x8 (&f)[Tile<D>::NC], const __bf16
 // read hands lane m element (m % 4) of the 8-byte row addressed by lane
 // 4*slot + m/4; lane m therefore addresses key (16*c2 + 8*x + 4*h + m/4) at
 // columns (32*t + 16*G + 4*(m%4)) .. +3, and receives column 32*t + 16*G + m
-// of the four keys 16*c2 + 8*x + 4*h + 0..3 -- matching P^T's key order.
+// of the four keys 16*c2 + 8*x + 4*h + 0..3 -- matching P^T's key order.  In the
+// tile layout those addresses are vo[x] + tile_offset(16 c2, 8 t) (VOps).
+struct VOps {
+  uint32_t vo[2];  // byte offsets of this lane's two reads at t = c2 = 0
+  __device__ __forceinline__ void init(int lane) {
+    const int m = lane & 15, G = (lane >> 4) & 1, h = lane >> 5;
+    const int ch = 2 * G + ((m & 3) >> 1);  // chunk within the 64-byte row segment
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = 8 * x + 4 * h + (m >> 2);
+      vo[x] = (uint32_t)(tile_offset(r, ch) + 8 * (m & 1));
+    }
+  }
+};
 template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const __bf16* vt, int t, int c2, int lane) {
-  const int m = lane & 15, G = (lane >> 4) & 1, h = lane >> 5;
-  const int col = 32 * t + 16 * G + 4 * (m & 3);
-  const int key0 = 16 * c2 + 4 * h + (m >> 2);
+__device__ __forceinline__ bf16x8 v_operand(const __bf16* vt, const VOps& vops, int t, int c2) {
   typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  const lds_shortx4* a0 = (const lds_shortx4*)(vt + key0 * Tile<D>::VSTRIDE + col);
-  const lds_shortx4* a1 = (const lds_shortx4*)(vt + (key0 + 8) * Tile<D>::VSTRIDE + col);
+  const char* base = reinterpret_cast<const char*>(vt) + tile_offset(16 * c2, 4 * t);
+  const lds_shortx4* a0 = (const lds_shortx4*)(base + vops.vo[0]);
+  const lds_shortx4* a1 = (const lds_shortx4*)(base + vops.vo[1]);
   shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_shortx4*>(a0));
   shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_shortx4*>(a1));
   short __attribute__((ext_vector_type(8))) both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, both);
 }
+
+// K fragment offsets of one lane (row i, half h) in the tile layout: MFMA step c
+// reads ko[c & 1] + tile_offset(0, 4 (c >> 1)).
+struct KOps {
+  uint32_t ko[2];
+  __device__ __forceinline__ void init(int i, int h) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) ko[c] = (uint32_t)tile_offset(i, qk_chunk(c, h));
+  }
+};
 
 // Q^T operand source: the query block's fragments held in registers.
 template <int D>
@@ -184,11 +219,13 @@ __device__ __forceinline__ float max_tree3(const float (&v)[K]) {
 // log-sum-exps of its scaled logits over keys 0..15 and 16..31 (log2 units) are
 // stored at blse + bidx[n] * 64 + {0, 32} + query, where the block-mass epilogue
 // reads them back.
-template <int D, int N, class QS, bool SUB = false, int BL = 0>
+// mid() runs once the score products are issued, while the matrix cores work
+// on them (the streaming loop issues the next trip's copies there).
+template <int D, int N, class QS, bool SUB = false, int BL = 0, class MID>
 __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* const (&kt)[N], const QS& qf,
                                              const __bf16* const (&vt)[N], const bool (&diag)[N], int i, int h,
-                                             int lane, float sl2, int sub_bits = 0xFF, float* blse = nullptr,
-                                             const int* bidx = nullptr) {
+                                             const KOps& kops, const VOps& vops, float sl2, int sub_bits,
+                                             float* blse, const int* bidx, MID&& mid) {
   using T = Tile<D>;
   floatx16 s[N];
 #pragma unroll
@@ -200,11 +237,15 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
   for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(kt[n] + i * T::KSTRIDE + h * T::HALF + 8 * c);
+      const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kt[n]) + kops.ko[c & 1] +
+                                                          tile_offset(0, 4 * (c >> 1)));
       s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf.get(c), s[n], 0, 0, 0);
     }
   }
   __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     if (diag[n]) {
@@ -278,7 +319,7 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
         st.acc[t] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], t, c2, lane), pb[c2], st.acc[t], 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], vops, t, c2), pb[c2], st.acc[t], 0, 0, 0);
   }
   st.l += lsum;
 }
@@ -442,9 +483,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // The block-mass sweep reuses buffer 0 for MTRIP K-only tiles per trip.
   using DT = DmaTrip<D, TRIP>;
   constexpr int MTRIP = 4;
-  typedef __bf16 KTile[32 * T::KSTRIDE];
-  static_assert(!MASS || MTRIP * sizeof(KTile) <= DT::BYTES, "sweep tiles fit buffer 0");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[DT::BYTES];
+  typedef __bf16 KTile[32 * T::SKSTRIDE];
+  constexpr size_t B0_BYTES = MASS && MTRIP * sizeof(KTile) > DT::BYTES ? MTRIP * sizeof(KTile) : DT::BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[B0_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_b1[DT::BYTES];
   KTile* const mk = reinterpret_cast<KTile*>(lds_b0);
   constexpr int MW = SUB ? kSubTileWords : kMaxMaskWords;  // row bitmask words
@@ -455,6 +496,10 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // uniform per wavefront (the compiler cannot tell that tid >> 6 is)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 31, h = lane >> 5;
+  KOps kops;
+  kops.init(i, h);
+  VOps vops;
+  vops.init(lane);
   const int ngroups = (a.nq + W - 1) / W;
   const int bhn = a.rows / a.nq;
   constexpr bool PLAN_ROWS = SPARSE && !SUB;  // rows may come from an execution plan
@@ -570,38 +615,27 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   }
 
   // Direct-to-LDS tile copies.  A trip buffer has 2 TRIP regions (the K and V
-  // tile of each of its tiles); with W >= 2 TRIP wavefronts, W / (2 TRIP) of
-  // them share a region, taking every (W / (2 TRIP))-th of its wave-copies;
-  // with fewer, each wavefront fills whole regions.  Which chunk of the source
-  // tile each lane fetches is fixed for the kernel; only the block numbers
-  // change per trip.
+  // tile of each of its tiles), D / 16 copies each; with W >= 2 TRIP
+  // wavefronts, W / (2 TRIP) of them share a region, taking every
+  // (W / (2 TRIP))-th of its copies; with fewer, each wavefront fills whole
+  // regions.  Copy x fills block x of the tile (tile_offset): lane j fetches row
+  // 16 (x % 2) + j / 4, chunk 4 (x / 2) + ((j % 4) ^ (j / 16 % 4)); the lane part
+  // of that source offset is fixed for the kernel, the rest is uniform.
   constexpr int NR = 2 * TRIP;                        // regions per trip buffer
   constexpr int WPR = W >= NR ? W / NR : 1;           // wavefronts per region
   constexpr int RPW = W >= NR ? 1 : NR / W;           // regions per wavefront
   static_assert(W >= NR ? W % NR == 0 : NR % W == 0, "regions and wavefronts");
-  constexpr int XS = (DT::VI > DT::KI ? DT::VI : DT::KI);
-  constexpr int S = (XS + WPR - 1) / WPR;             // copies per region and wavefront, at most
-  const int sub = wave / NR;                          // W >= NR: this wavefront's share of its region
-  uint32_t voff[RPW][S];                              // lane's byte offset within the source tile
-#pragma unroll
-  for (int k = 0; k < RPW; ++k) {
-    const int r = W >= NR ? wave % NR : wave + W * k;  // region: tile r % TRIP, V if r >= TRIP
-    const bool isv = r >= TRIP;
-#pragma unroll
-    for (int c = 0; c < S; ++c) {
-      const int p = 64 * (sub + WPR * c) + lane;  // chunk of the padded tile region
-      const int row = isv ? p / DT::CV : p / DT::CK, ch = isv ? p % DT::CV : p % DT::CK;
-      // chunks past a row's data (padding) and past the tile re-read chunk 0
-      voff[k][c] = row < 32 && ch < T::C8 ? (uint32_t)(row * D + ch * 8) * 2u : 0u;
-    }
-  }
+  constexpr int S = (DT::CI + WPR - 1) / WPR;         // copies per region and wavefront, at most
+  const int sub = W >= NR ? wave / NR : 0;            // this wavefront's share of its region
+  const uint32_t lane_src = (uint32_t)((lane >> 2) * (2 * D) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
   // buffer resources over this head's K and V (out-of-range reads return 0)
   const uint32_t kv_bytes = (uint32_t)a.seqlen * (uint32_t)(D * 2);
   const u32x4 rsk = buffer_resource(kh, kv_bytes), rsv = buffer_resource(vh, kv_bytes);
   auto issue = [&](unsigned char* buf, const int (&c)[TRIP]) {
+    const uint32_t lb = lds_address(buf);
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
-      const int r = W >= NR ? wave % NR : wave + W * k;
+      const int r = W >= NR ? wave % NR : wave + W * k;  // region: tile r % TRIP, V if r >= TRIP
       const bool isv = r >= TRIP;
       const int u = isv ? r - TRIP : r;
       int e = c[0];
@@ -609,21 +643,17 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       for (int t = 1; t < TRIP; ++t)
         if (u == t) e = c[t];
       if (e < 0) continue;
-      unsigned char* dst = buf + (isv ? TRIP * DT::KB + u * DT::VB : u * DT::KB);
-      const int soff = (e >> kEntryShift) * (32 * D * 2);
-      if (isv) {
+      const uint32_t dst = lb + (uint32_t)(isv ? TRIP * DT::KB + u * DT::VB : u * DT::KB);
+      const uint32_t tile = (uint32_t)(e >> kEntryShift) * (uint32_t)DT::KB;
 #pragma unroll
-        for (int cc = 0; cc < S; ++cc) {
-          const int x = sub + WPR * cc;
-          if (x < DT::VI)
-            copy_to_lds(rsv, dst + 1024 * x, voff[k][cc], soff);
-        }
-      } else {
-#pragma unroll
-        for (int cc = 0; cc < S; ++cc) {
-          const int x = sub + WPR * cc;
-          if (x < DT::KI)
-            copy_to_lds(rsk, dst + 1024 * x, voff[k][cc], soff);
+      for (int cc = 0; cc < S; ++cc) {
+        const int x = sub + WPR * cc;
+        if (DT::CI % WPR == 0 || x < DT::CI) {
+          const uint32_t soff = tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64);
+          if (isv)
+            copy_to_lds(rsv, dst + 1024 * x, lane_src, soff);
+          else
+            copy_to_lds(rsk, dst + 1024 * x, lane_src, soff);
         }
       }
     }
@@ -634,9 +664,10 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     return active && (!SPARSE || ((e >> wave) & 1)) && (e >> kEntryShift) <= qb;
   };
 
-  // Runs `work(buffer, entries)` over the list, TRIP blocks per trip, with two
-  // trip buffers: while one trip is computed, the next one's copies run into the
-  // other buffer.  One barrier per trip, after each wavefront has waited for its
+  // Runs `work(buffer, entries, issue_next)` over the list, TRIP blocks per trip,
+  // with two trip buffers: while one trip is computed, the next one's copies
+  // run into the other buffer (work calls issue_next exactly once, after its
+  // first score products, or at once when it has no tile in the trip).  One barrier per trip, after each wavefront has waited for its
   // own copies: then the next trip's tiles are complete and every wavefront is
   // done with the buffer the trip after it will overwrite.
   auto fetch = [&](auto& list, int (&c)[TRIP], bool more) {
@@ -655,13 +686,13 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     while (c0[0] >= 0) {
       fetch(list, c1, c0[TRIP - 1] >= 0);
       issue(lds_b1, c1);
-      work(lds_b0, c0);
+      work(lds_b0, c0, [] {});
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (c1[0] < 0) break;
       fetch(list, c0, c1[TRIP - 1] >= 0);
       issue(lds_b0, c0);
-      work(lds_b1, c1);
+      work(lds_b1, c1, [] {});
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
     }
@@ -685,7 +716,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     return (int)((__builtin_amdgcn_readfirstlane(sm[0]) >> sh) & 3u) |
            (int)(((__builtin_amdgcn_readfirstlane(sm[kSubWords]) >> sh) & 3u) << 2);
   };
-  auto attend = [&](const unsigned char* buf, const int (&c)[TRIP]) {
+  auto attend = [&](const unsigned char* buf, const int (&c)[TRIP], auto&& issue_next) {
     const __bf16* const kb = reinterpret_cast<const __bf16*>(buf);  // K tile u at kb + u * KE
     const __bf16* const vb = reinterpret_cast<const __bf16*>(buf + TRIP * DT::KB);
     constexpr int KE = DT::KB / 2, VE = DT::VB / 2;
@@ -695,6 +726,14 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       if (c[u] >= 0 && member(c[u])) mine |= 1 << u;
       if ((c[u] >> kEntryShift) == qb) dg |= 1 << u;
     }
+    bool issued = mine == 0;
+    if (issued) issue_next();
+    auto once = [&] {
+      if (!issued) {
+        issue_next();
+        issued = true;
+      }
+    };
     while (__builtin_popcount(mine) >= 2) {
       const int u0 = __builtin_ctz(mine);
       mine &= mine - 1;
@@ -704,8 +743,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const __bf16* const vp[2] = {vb + u0 * VE, vb + u1 * VE};
       const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
       const int bi[2] = {c[u0] >> kEntryShift, c[u1] >> kEntryShift};
-      attend_tiles<D, 2, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2,
-                                            sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi);
+      attend_tiles<D, 2, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, kops, vops, a.scale_log2,
+                                            sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi, once);
     }
     while (mine) {
       const int u0 = __builtin_ctz(mine);
@@ -714,8 +753,8 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const __bf16* const vp[1] = {vb + u0 * VE};
       const bool dp[1] = {((dg >> u0) & 1) != 0};
       const int bi[1] = {c[u0] >> kEntryShift};
-      attend_tiles<D, 1, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, lane, a.scale_log2, sub4(bi[0]) | 0xF0,
-                                            blse, bi);
+      attend_tiles<D, 1, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, kops, vops, a.scale_log2, sub4(bi[0]) | 0xF0,
+                                            blse, bi, once);
     }
   };
   if (use_plan) {
@@ -804,7 +843,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
         for (int u = 0; u < CPT; ++u) {
           const int c = tid + NTHR * u;
           if (CHUNKS % NTHR == 0 || c < CHUNKS)
-            *reinterpret_cast<bf16x8*>(&mk[buf][(c / T::C8) * T::KSTRIDE + (c % T::C8) * 8]) = r[u];
+            *reinterpret_cast<bf16x8*>(&mk[buf][(c / T::C8) * T::SKSTRIDE + (c % T::C8) * 8]) = r[u];
         }
       };
       int c[MTRIP];
@@ -848,7 +887,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       for (int cc = 0; cc < T::NC; ++cc)
 #pragma unroll
         for (int buf = 0; buf < MTRIP; ++buf) {
-          const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&mk[buf][i * T::KSTRIDE + h * T::HALF + 8 * cc]);
+          const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&mk[buf][i * T::SKSTRIDE + 8 * qk_chunk(cc, h)]);
           sv[buf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf.get(cc), sv[buf], 0, 0, 0);
         }
       __builtin_amdgcn_s_setprio(0);
