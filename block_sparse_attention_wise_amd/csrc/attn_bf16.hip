@@ -303,9 +303,15 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
       float x1 = ((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15]));
       lsum += x0 + x1;
       if (blse != nullptr) {
-        x0 = halves_sum(x0);
-        x1 = halves_sum(x1);
-        blse[bidx[n] * kMassWsSlot + 32 * h + i] = __builtin_amdgcn_logf(h ? x1 : x0) + m_use;
+        if constexpr (BL == 32) {
+          // one value per query: the whole tile's sum
+          const float x = halves_sum(x0 + x1);
+          if (h == 0) blse[bidx[n] * mass_ws_slot(32) + i] = __builtin_amdgcn_logf(x) + m_use;
+        } else {
+          x0 = halves_sum(x0);
+          x1 = halves_sum(x1);
+          blse[bidx[n] * mass_ws_slot(16) + 32 * h + i] = __builtin_amdgcn_logf(h ? x1 : x0) + m_use;
+        }
       }
     } else {
 #pragma unroll
@@ -704,7 +710,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // triangle of key tiles 0..qb per (batch, head) row
   float* const blse = MASS && a.mass_ws != nullptr && active
                           ? a.mass_ws + ((size_t)bh * ((size_t)a.nq * (a.nq + 1) / 2) + (size_t)qb * (qb + 1) / 2) *
-                                            kMassWsSlot
+                                            mass_ws_slot(BL)
                           : nullptr;
   // a trip's tiles of this wavefront's row, two per softmax step
   // 16-token blocks: which 16 x 16 sub-blocks of tile b this wavefront's two rows
@@ -779,10 +785,11 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     // log-sum-exp of query i's scaled logits over the keys of block b (j <= i)
     // and lse_i the row's, r_qb = (1/B) sum_{i in q} exp(L_ib - lse_i) (log2
     // units here).  Lane l takes key tile b = l (+ 64 per pass): it reads the
-    // tile's 32 (B = 32) or 64 (B = 16: per query, keys 0..15 then 16..31)
-    // stored values in one burst and sums over the queries itself.
+    // tile's 32 (B = 32: per query, all 32 keys) or 64 (B = 16: per query, keys
+    // 0..15 then 16..31) stored values in one burst and sums over the queries
+    // itself.
     constexpr bool B16 = MODE == kDenseMass16;
-    constexpr int SLOT = kMassWsSlot;
+    constexpr int SLOT = mass_ws_slot(B16 ? 16 : 32);
     const int nm = B16 ? 2 * a.nq : a.nq;  // mass row length
     if (active) {
       float* mrow = a.mass + (size_t)(bh * a.nq + qb) * (B16 ? 4 * a.nq : a.nq);

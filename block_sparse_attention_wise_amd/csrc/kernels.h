@@ -64,11 +64,11 @@ hipError_t launch_attn_bf16(const AttnBf16Args& a, int head_dim, bool sparse, bo
 hipError_t launch_attn_f32(const AttnF32Args& a, int head_dim, bool sparse, bool mass, bool b16,
                            hipStream_t stream);
 size_t support_workspace_bytes(int bh, int nq);
-// floats of the one-pass block-mass store per (query block, key tile) pair (one
-// per query and 16-key half, at either block size), and its total size for bh
-// rows of nq tiles
-constexpr int kMassWsSlot = 64;
-size_t mass_ws_bytes(int64_t bh, int nq);
+// floats of the one-pass block-mass store per (query block, key tile) pair: one
+// per query at block size 32, one per query and 16-key half at block size 16;
+// and its total size for bh rows of nq tiles
+__host__ __device__ constexpr int mass_ws_slot(int block) { return block == 16 ? 64 : 32; }
+size_t mass_ws_bytes(int64_t bh, int nq, int block);
 size_t plan_capacity(int bh, int nq);
 // kind: 0 cumulative-eta support per step, unioned over the steps; 1 SizeMatched and
 // 2 MassMatched against the reference schedule (steps == 1)

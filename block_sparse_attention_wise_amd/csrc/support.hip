@@ -677,7 +677,7 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   // group cap relative to the longest row's cost: 9/10 for the head_dim 64
   // kernel (three workgroups per CU, more slots than groups, so the longest
   // groups decide its end), 5/4 for the others
-  const int cap_num = plan_head_dim == 64 ? 9 : 5, cap_den = plan_head_dim == 64 ? 10 : 4;
+  const int cap_num = plan_head_dim == 64 ? 9 : 3, cap_den = plan_head_dim == 64 ? 10 : 2;
   hipLaunchKernelGGL(group_rows_kernel, dim3(bh), dim3(kGroupThreads), 0, stream, masks, counts, max_count, nq,
                      nwords, gh, cap_num, cap_den, plan_rows);
   e = hipGetLastError();

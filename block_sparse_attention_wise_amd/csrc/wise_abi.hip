@@ -88,8 +88,8 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
 
 }  // namespace
 
-size_t mass_ws_bytes(int64_t bh, int nq) {
-  return (size_t)bh * ((size_t)nq * (nq + 1) / 2) * kMassWsSlot * sizeof(float);
+size_t mass_ws_bytes(int64_t bh, int nq, int block) {
+  return (size_t)bh * ((size_t)nq * (nq + 1) / 2) * mass_ws_slot(block) * sizeof(float);
 }
 
 }  // namespace wise
@@ -115,7 +115,7 @@ size_t wise_full_attn_mass_workspace_bytes(int batch, int heads, int seqlen, int
   if (block != kBlock && block != kBlock / 2) return 0;
   const int64_t bh = (int64_t)batch * heads;
   if (bh * (seqlen / block) > INT32_MAX) return 0;
-  return mass_ws_bytes(bh, seqlen / kBlock);
+  return mass_ws_bytes(bh, seqlen / kBlock, block);
 }
 
 wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim,
