@@ -219,13 +219,11 @@ __device__ __forceinline__ float max_tree3(const float (&v)[K]) {
 // log-sum-exps of its scaled logits over keys 0..15 and 16..31 (log2 units) are
 // stored at blse + bidx[n] * 64 + {0, 32} + query, where the block-mass epilogue
 // reads them back.
-// mid() runs once the score products are issued, while the matrix cores work
-// on them (the streaming loop issues the next trip's copies there).
-template <int D, int N, class QS, bool SUB = false, int BL = 0, class MID>
+template <int D, int N, class QS, bool SUB = false, int BL = 0>
 __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* const (&kt)[N], const QS& qf,
                                              const __bf16* const (&vt)[N], const bool (&diag)[N], int i, int h,
                                              const KOps& kops, const VOps& vops, float sl2, int sub_bits,
-                                             float* blse, const int* bidx, MID&& mid) {
+                                             float* blse, const int* bidx) {
   using T = Tile<D>;
   floatx16 s[N];
 #pragma unroll
@@ -243,9 +241,6 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
     }
   }
   __builtin_amdgcn_s_setprio(0);
-  __builtin_amdgcn_sched_barrier(0);
-  mid();
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     if (diag[n]) {
@@ -410,6 +405,15 @@ constexpr int stream_waves() {
 struct DenseList {
   int b, nb;
   __device__ __forceinline__ int next() { return b < nb ? (b++ << kEntryShift) | 0xFF : -1; }
+  // the next trip's T entries (-1: none); false once the list is exhausted
+  template <int T>
+  __device__ __forceinline__ bool next_trip(int (&c)[T]) {
+    if (b >= nb) return false;
+#pragma unroll
+    for (int u = 0; u < T; ++u) c[u] = b + u < nb ? ((b + u) << kEntryShift) | 0xFF : -1;
+    b += T;
+    return true;
+  }
 };
 // union of the workgroup's W rows, ascending, from their bitmasks in LDS
 template <int W, int MW>
@@ -438,31 +442,52 @@ struct UnionList {
     for (int r = 0; r < W; ++r) m |= ((row_word(r, wd) >> bit) & 1u) << r;
     return ((32 * wd + bit) << kEntryShift) | m;
   }
+  template <int T>
+  __device__ __forceinline__ bool next_trip(int (&c)[T]) {
+    bool more = true;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      c[t] = more ? next() : -1;
+      more = c[t] >= 0;
+    }
+    return c[0] >= 0;
+  }
 };
-// a precomputed execution plan (wise_build_support): entries in trip order,
-// read 64 at a time, one per lane; entries naming a block past the group's last
-// query block, or with no row, are skipped.  The first chunk is loaded up to
-// the group's slot end (limit) before the entry count is known.
+// a precomputed execution plan (wise_build_support): the group's entries in
+// trip order, 64 per chunk, one per lane, read with readlane; the next chunk is
+// loaded while the current one is read.  Entries naming a block past the
+// group's last query block, or with no row, become holes (-1).
 struct PlanList {
   const int32_t* e;
   int base, end, qlast, lane;
-  int cur;
-  int idx;  // next entry within the current chunk
-  __device__ __forceinline__ void load_chunk(int limit) {
-    cur = base + lane < limit ? e[base + lane] : -1;
+  int cur, nxt;  // entries base .. base + 63 and the 64 after them
+  int idx;       // next entry within the current chunk
+  __device__ __forceinline__ int load(int at) const { return at + lane < end ? e[at + lane] : -1; }
+  __device__ __forceinline__ void start(int first, int count) {
+    base = first;
+    end = first + count;
     idx = 0;
+    cur = load(base);
+    nxt = load(base + 64);
   }
-  __device__ __forceinline__ int next() {
-    for (;;) {
-      if (idx == 64) {
-        base += 64;
-        if (base >= end) return -1;
-        load_chunk(end);
-      }
-      if (base + idx >= end) return -1;
-      const int v = __builtin_amdgcn_readlane(cur, idx++);
-      if (v >= 0 && (v >> kEntryShift) <= qlast && (v & 0xFF) != 0) return v;
+  __device__ __forceinline__ int entry(int at) const {
+    const int v = base + at < end ? __builtin_amdgcn_readlane(cur, at) : -1;
+    return v >= 0 && (v >> kEntryShift) <= qlast && (v & 0xFF) != 0 ? v : -1;
+  }
+  template <int T>
+  __device__ __forceinline__ bool next_trip(int (&c)[T]) {
+    static_assert(64 % T == 0, "trips do not straddle chunks");
+    if (base + idx >= end) return false;
+    if (idx == 64) {
+      base += 64;
+      idx = 0;
+      cur = nxt;
+      nxt = load(base + 64);
     }
+#pragma unroll
+    for (int u = 0; u < T; ++u) c[u] = entry(idx + u);
+    idx += T;
+    return true;
   }
 };
 
@@ -565,15 +590,13 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * (active ? qb : qlast) + i) * D, h);
   // sparse mode with an execution plan: group g's entry count plan[g] and its
   // first entries (fixed slot of nq entries) load together with Q
-  PlanList plist{nullptr, 0, 0, qlast, lane, -1, 64};
+  PlanList plist{nullptr, 0, 0, qlast, lane, -1, -1, 0};
   if (use_plan) {
     const int groups = bhn * plan_groups_per_head(a.nq), g = pgroup;
     const int slot = g * a.nq;  // plan capacity (checked on the host) covers every slot
     plist.e = a.plan + groups + 1 + kPlanRows * groups;
-    plist.base = slot;
-    plist.load_chunk(slot + a.nq);
     const int cnt = a.plan[g];
-    plist.end = slot + (cnt < 0 ? 0 : (cnt > a.nq ? a.nq : cnt));
+    plist.start(slot, cnt < 0 ? 0 : (cnt > a.nq ? a.nq : cnt));
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
@@ -670,37 +693,31 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     return active && (!SPARSE || ((e >> wave) & 1)) && (e >> kEntryShift) <= qb;
   };
 
-  // Runs `work(buffer, entries, issue_next)` over the list, TRIP blocks per trip,
-  // with two trip buffers: while one trip is computed, the next one's copies
-  // run into the other buffer (work calls issue_next exactly once, after its
-  // first score products, or at once when it has no tile in the trip).  One barrier per trip, after each wavefront has waited for its
+  // Runs `work(buffer, entries)` over the list, TRIP blocks per trip, with two
+  // trip buffers: while one trip is computed, the next one's copies run into the
+  // other buffer.  One barrier per trip, after each wavefront has waited for its
   // own copies: then the next trip's tiles are complete and every wavefront is
-  // done with the buffer the trip after it will overwrite.
-  auto fetch = [&](auto& list, int (&c)[TRIP], bool more) {
-#pragma unroll
-    for (int u = 0; u < TRIP; ++u) {
-      c[u] = more ? list.next() : -1;
-      more = c[u] >= 0;
-    }
-  };
+  // done with the buffer the trip after it will overwrite.  The lists are
+  // wavefront-uniform, so every wavefront takes the same number of trips.
   auto stream = [&](auto& list, auto&& work) {
     int c0[TRIP], c1[TRIP];
-    fetch(list, c0, true);
+    if (!list.next_trip(c0)) return;
     issue(lds_b0, c0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    while (c0[0] >= 0) {
-      fetch(list, c1, c0[TRIP - 1] >= 0);
-      issue(lds_b1, c1);
-      work(lds_b0, c0, [] {});
+    for (;;) {
+      const bool more1 = list.next_trip(c1);
+      if (more1) issue(lds_b1, c1);
+      work(lds_b0, c0);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      if (c1[0] < 0) break;
-      fetch(list, c0, c1[TRIP - 1] >= 0);
-      issue(lds_b0, c0);
-      work(lds_b1, c1, [] {});
+      if (!more1) break;
+      const bool more0 = list.next_trip(c0);
+      if (more0) issue(lds_b0, c0);
+      work(lds_b1, c1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
+      if (!more0) break;
     }
   };
 
@@ -722,7 +739,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     return (int)((__builtin_amdgcn_readfirstlane(sm[0]) >> sh) & 3u) |
            (int)(((__builtin_amdgcn_readfirstlane(sm[kSubWords]) >> sh) & 3u) << 2);
   };
-  auto attend = [&](const unsigned char* buf, const int (&c)[TRIP], auto&& issue_next) {
+  auto attend = [&](const unsigned char* buf, const int (&c)[TRIP]) {
     const __bf16* const kb = reinterpret_cast<const __bf16*>(buf);  // K tile u at kb + u * KE
     const __bf16* const vb = reinterpret_cast<const __bf16*>(buf + TRIP * DT::KB);
     constexpr int KE = DT::KB / 2, VE = DT::VB / 2;
@@ -732,14 +749,6 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       if (c[u] >= 0 && member(c[u])) mine |= 1 << u;
       if ((c[u] >> kEntryShift) == qb) dg |= 1 << u;
     }
-    bool issued = mine == 0;
-    if (issued) issue_next();
-    auto once = [&] {
-      if (!issued) {
-        issue_next();
-        issued = true;
-      }
-    };
     while (__builtin_popcount(mine) >= 2) {
       const int u0 = __builtin_ctz(mine);
       mine &= mine - 1;
@@ -750,7 +759,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
       const int bi[2] = {c[u0] >> kEntryShift, c[u1] >> kEntryShift};
       attend_tiles<D, 2, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, kops, vops, a.scale_log2,
-                                            sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi, once);
+                                            sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi);
     }
     while (mine) {
       const int u0 = __builtin_ctz(mine);
@@ -760,7 +769,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       const bool dp[1] = {((dg >> u0) & 1) != 0};
       const int bi[1] = {c[u0] >> kEntryShift};
       attend_tiles<D, 1, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, kops, vops, a.scale_log2, sub4(bi[0]) | 0xF0,
-                                            blse, bi, once);
+                                            blse, bi);
     }
   };
   if (use_plan) {

@@ -29,7 +29,8 @@ __device__ __forceinline__ float group8_sum(float x) {
   return x + __shfl_xor(x, 4);
 }
 
-constexpr int kSubWords32 = 64;  // 16-token sparse rows: 2 * nq <= 2048
+constexpr int kSubWords32 = 64;   // 16-token sparse rows: 2 * nq <= 2048
+constexpr int kRowWords32 = 128;  // 32-token sparse rows: nq <= 4096
 
 template <int D, bool SPARSE, bool MASS, bool B16>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
@@ -41,6 +42,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   __shared__ float ps[32 * 33];
   __shared__ float red[8];
   __shared__ uint32_t smask[B16 && SPARSE ? 2 * kSubWords32 : 1];  // the two 16-token rows
+  __shared__ uint32_t rmask[!B16 && SPARSE ? kRowWords32 : 1];      // the 32-token row
 
   const int tid = threadIdx.x;
   const int qi = tid >> 3, sub = tid & 7;
@@ -73,11 +75,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
     }
     __syncthreads();
   } else if (SPARSE) {
+    // the row as a bitmask over key blocks 0..qb: entries outside that range
+    // are ignored and a block listed twice counts once
+    for (int w = tid; w <= (qb >> 5); w += 256) rmask[w] = 0u;
+    __syncthreads();
     int64_t b0 = a.row_ptr[row], b1 = a.row_ptr[row + 1];
     b0 = b0 < 0 ? 0 : (b0 > a.col_cap ? a.col_cap : b0);
     b1 = b1 < b0 ? b0 : (b1 > a.col_cap ? a.col_cap : b1);
-    beg = (int)b0;
-    end = (int)b1;
+    for (int64_t e = b0 + tid; e < b1; e += 256) {
+      const int b = a.col_idx[e];
+      if (b >= 0 && b <= qb) atomicOr(&rmask[b >> 5], 1u << (b & 31));
+    }
+    __syncthreads();
   }
 
   float acc[NU];
@@ -87,8 +96,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
   const int qrow = 32 * qb + qi;
 
   for (int it = beg; it < end; ++it) {
-    const int b = SPARSE && !B16 ? a.col_idx[it] : it;
-    if (SPARSE && !B16 && (b < 0 || b > qb)) continue;
+    const int b = it;
+    if (SPARSE && !B16 && !((rmask[b >> 5] >> (b & 31)) & 1u)) continue;  // uniform over the workgroup
     // B16: which 16 x 16 sub-blocks of tile b are scheduled (bit 2 x + kh)
     int subm = 0xF;
     if (SPARSE && B16) {

@@ -10,7 +10,7 @@ namespace wise {
 namespace {
 
 constexpr int kBlock = 32;              // the kernels' query and key tile
-constexpr int kMaxSparseBlocks = 4096;  // bf16 sparse kernel: key tiles per row bitmask
+constexpr int kMaxSparseBlocks = 4096;  // sparse kernels: key tiles per row bitmask
 constexpr int kMaxSparseBlocks16 = 2048;  // ... 16-token key blocks per row
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -247,7 +247,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
   if (st != WISE_OK) return st;
   if (!row_ptr || !col_idx || col_capacity < 0) return WISE_ERR_INVALID_ARG;
   if (!aligned4(row_ptr) || !aligned4(col_idx)) return WISE_ERR_INVALID_ARG;
-  if (dt == WISE_BF16 && seqlen / kBlock > kMaxSparseBlocks) return WISE_ERR_UNSUPPORTED;
+  if (seqlen / kBlock > kMaxSparseBlocks) return WISE_ERR_UNSUPPORTED;
   // 16-token rows are bitmasks of 2048 blocks in both kernels' LDS
   if (block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
   if (plan != nullptr) {

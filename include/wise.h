@@ -284,9 +284,9 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  * counts outside 0..nq are ignored (clamped).  In the CSR a block listed twice counts once; a plan must come
  * from wise_build_support, which lists each block of a group once.  A row left
  * with no admissible key writes o = 0 and lse = -inf (wise_build_support never
- * produces one).  The bf16 kernel supports up to 4096 key blocks per head
- * (seqlen <= 131072), and both kernels up to 2048 at block 16 (seqlen <=
- * 32768); beyond that WISE_ERR_UNSUPPORTED is returned.
+ * produces one).  Both kernels support up to 4096 key blocks per head
+ * (seqlen <= 131072), and up to 2048 at block 16 (seqlen <= 32768); beyond
+ * that WISE_ERR_UNSUPPORTED is returned.
  */
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
                              int head_dim, int block, const void* q, const void* k, const void* v, void* o,

@@ -129,10 +129,11 @@ def sorted_order(masses):
 def select_support(masses, eta):
     """Cumulative-eta block support of one (head, query block, step).
 
-    The WISE paper, §3 ("the smallest set of admissible keys whose cumulative
-    attention mass ... is at least eta") applied to the block masses of §5.1: the
-    smallest set is a prefix of the blocks sorted by mass, so sort, take the
-    float64 running sum c_k, and keep the first k* = min{k : c_k >= eta} blocks.
+    The support of the WISE paper, §3 -- the fewest admissible blocks whose
+    masses add up to eta or more -- taken over the block masses of §5.1.  Such a
+    minimal set is always a prefix of the blocks ordered by decreasing mass, so
+    sort, form the float64 running sum c_k, and keep the first
+    k* = min{k : c_k >= eta} blocks.
 
     masses: the q+1 admissible block masses r_q0 .. r_qq.
     Returns the selected block indices, ascending.

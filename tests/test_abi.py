@@ -85,11 +85,12 @@ def test_mass_workspace_bytes(lib):
     f = lib.wise_full_attn_mass_workspace_bytes
     assert f(0, 1, 64, 32) == 0 and f(1, 0, 64, 32) == 0 and f(1, 1, 0, 32) == 0
     assert f(1, 1, 48, 32) == 0 and f(1, 1, 64, 64) == 0 and f(1, 1, 64, 8) == 0
-    # the causal triangle of 32 x 32 tiles, 64 floats per tile (per query and 16-key half)
+    # the causal triangle of 32 x 32 tiles: 32 floats per tile at block 32 (one per
+    # query), 64 at block 16 (one per query and 16-key half)
     for b, h, n in ((1, 1, 32), (2, 3, 128), (1, 32, 4096)):
         nt = n // 32
-        assert f(b, h, n, 32) == 4 * b * h * nt * (nt + 1) // 2 * 64
-        assert f(b, h, n, 16) == f(b, h, n, 32)
+        assert f(b, h, n, 32) == 4 * b * h * nt * (nt + 1) // 2 * 32
+        assert f(b, h, n, 16) == 2 * f(b, h, n, 32)
 
 
 def test_mass_workspace_validation(lib):

@@ -247,11 +247,12 @@ def test_sparse_ignores_invalid_entries_and_handles_empty_rows(dtype):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     n, d, nq = 128, 128, 4
     q, k, v = (torch.from_numpy(rng.standard_normal((1, 1, n, d)).astype(np.float32)).to(tdt) for _ in range(3))
-    # row 0 empty; row 1 lists b > q and negative; row 2 unsorted with an out-of-range id; row 3 normal
-    rp = np.array([0, 0, 4, 8, 10], dtype=np.int32)
-    ci = np.array([3, 1, -5, 0, 2, 99, 0, 7, 0, 3], dtype=np.int32)
+    # row 0 empty; row 1 lists b > q and negative; row 2 unsorted with an out-of-range id;
+    # row 3 lists each of its blocks twice (a block listed twice counts once)
+    rp = np.array([0, 0, 4, 8, 12], dtype=np.int32)
+    ci = np.array([3, 1, -5, 0, 2, 99, 0, 7, 0, 3, 3, 0], dtype=np.int32)
     sched = wise.Schedule(torch.from_numpy(rp).to(DEV), torch.from_numpy(ci).to(DEV),
-                          torch.tensor([10], dtype=torch.int32, device=DEV), 1, nq)
+                          torch.tensor([12], dtype=torch.int32, device=DEV), 1, nq)
     note(f"sparse invalid entries {dtype}")
     o = torch.full((1, 1, n, d), float("nan"), dtype=tdt, device=DEV)
     lse = torch.full((1, 1, n), float("nan"), dtype=torch.float32, device=DEV)
