@@ -2,6 +2,7 @@
 // host code, no HIP call before it passes), launch selection and status codes.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "wise.h"
@@ -86,6 +87,26 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
   return WISE_OK;
 }
 
+// Scratch of wise_build_support_static: one copy per GPU, resolved to a device
+// address once per device (with that device current) and kept per device.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[WISE_STATIC_SCRATCH_BYTES];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+wise_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WISE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return WISE_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return WISE_OK;
+}
+
 }  // namespace
 
 size_t mass_ws_bytes(int64_t bh, int nq, int block) {
@@ -165,6 +186,19 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
   hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, 0, nullptr, nullptr, 0, row_ptr, col_idx, nnz,
                                 plan, plan_head_dim, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
+}
+
+wise_status wise_build_support_static(int bh, int nq, int num_steps, const float* mass, float eta,
+                                      int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
+                                      int32_t* plan, int64_t plan_capacity, int plan_head_dim, void* stream) {
+  const size_t need = wise_build_support_workspace_bytes(bh, nq, num_steps);
+  if (need == 0) return WISE_ERR_INVALID_ARG;
+  if (need > WISE_STATIC_SCRATCH_BYTES) return WISE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const wise_status st = static_scratch(&ws);
+  if (st != WISE_OK) return st;
+  return wise_build_support(bh, nq, num_steps, mass, eta, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
+                            plan_head_dim, ws, need, stream);
 }
 
 size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps, int block) {

@@ -19,13 +19,13 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes",
     "wise_dense_attn",
     "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity", "wise_build_support",
     "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
-    "wise_build_support_blocked_workspace_bytes", "wise_build_support_blocked",
+    "wise_build_support_blocked_workspace_bytes", "wise_build_support_blocked", "wise_build_support_static",
 )
 
 
@@ -63,6 +63,8 @@ def _load():
                                                vp, ctypes.c_size_t, vp]
     lib.wise_retained_mass.restype = i32
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
+    lib.wise_build_support_static.restype = i32
+    lib.wise_build_support_static.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp]
     lib.wise_sparse_attn.restype = i32
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
                                      f32, vp]
@@ -259,6 +261,25 @@ def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspa
                                         *_plan_args(schedule), int(plan_head_dim), _ptr(workspace), workspace.numel(),
                                         _stream(stream))
     _check(st, "wise_build_support_blocked" if block != BLOCK else "wise_build_support")
+    return schedule
+
+
+def build_support_static(mass, eta: float, *, schedule: Schedule | None = None, stream=None,
+                         with_plan: bool = True, plan_head_dim: int = 0):
+    """build_support at block 32 through wise_build_support_static, which takes
+    no workspace and allocates nothing (its scratch is the library's own device
+    array); the schedule buffers are the caller's, as always."""
+    if mass.dim() != 4 or mass.shape[2] != mass.shape[3]:
+        raise ValueError("mass must be [num_steps, batch*heads, nq, nq]")
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
+        raise ValueError("mass must be a contiguous float32 device tensor")
+    steps, bh, nq, _ = mass.shape
+    if schedule is None:
+        schedule = alloc_schedule(bh, nq, mass.device, with_plan=with_plan)
+    st = lib.wise_build_support_static(bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
+                                       _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
+                                       *_plan_args(schedule), int(plan_head_dim), _stream(stream))
+    _check(st, "wise_build_support_static")
     return schedule
 
 

@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 8
+#define WISE_ABI_VERSION 9
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -166,13 +166,13 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 entry is (key block << 8) | membership, bit w of the
  *                 membership set iff the group's query block w lists that key
  *                 block.  Each key block of the group's union appears once, in
- *                 runs of 4 (the tiles the kernel holds at once) that spread
+ *                 runs of 2 (the tiles the kernel holds at once) that spread
  *                 the member rows' blocks evenly.
  *   plan_head_dim: the head dimension of the bf16 sparse attention that will
  *                 walk the plan (64, 96 or 128), or 0 if not known; it sets the
  *                 group cap: 9/10 of the longest row's cost at 64 (three
  *                 workgroups per CU there, so the longest groups decide the
- *                 kernel's end), 5/4 otherwise.  Any value gives a valid plan
+ *                 kernel's end), 3/2 otherwise.  Any value gives a valid plan
  *                 for every head dimension; others than these four are
  *                 rejected when plan is not NULL, ignored when it is.
  *   workspace   : device scratch of at least
@@ -184,6 +184,26 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                int32_t* nnz, int32_t* plan, int64_t plan_capacity, int plan_head_dim,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wise_build_support without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its scratch is a file-scope device array
+ * of WISE_STATIC_SCRATCH_BYTES (8 MiB) that every GPU the library runs on holds
+ * until the process ends; this call allocates nothing.  Calls on one GPU share
+ * that array: calls that overlap on one GPU (different streams, or threads)
+ * race and must be serialised by the caller.  Every byte of scratch the build
+ * reads it first writes in the same call, so nothing carries over between calls.
+ * Arguments and results as for wise_build_support; shapes whose workspace
+ * (wise_build_support_workspace_bytes) exceeds WISE_STATIC_SCRATCH_BYTES return
+ * WISE_ERR_UNSUPPORTED (bh up to 240 at nq = 512, 3276 at nq = 128),
+ * and WISE_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define WISE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+wise_status wise_build_support_static(int bh, int nq, int num_steps, const float* mass, float eta,
+                                      int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                      int32_t* nnz, int32_t* plan, int64_t plan_capacity, int plan_head_dim,
+                                      void* stream);
 
 /*
  * Working-set schedule selected at a coarser block size (the block-size study of

@@ -63,13 +63,14 @@ def test_every_declared_symbol_is_exported(lib):
                           "wise_build_support_workspace_bytes", "wise_build_support_plan_capacity",
                           "wise_build_support_variant", "wise_retained_mass", "wise_sparse_attn",
                           "wise_build_support_blocked", "wise_build_support_blocked_workspace_bytes",
+                          "wise_build_support_static",
                           "wise_status_string", "wise_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in wise.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 8
+    assert lib.wise_abi_version() == 9
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -248,3 +249,19 @@ def test_blocked_builder_validation(lib):
     assert blk(nq=9) == INVALID                 # not a whole number of 64-token blocks
     assert blk(wsb=f(2, 8, 4, 64) - 1) == INVALID
     assert blk(eta=0.0) == INVALID and blk(cap=10) == INVALID
+
+
+def test_static_builder_rejects_shapes_beyond_its_scratch(lib):
+    """The no-allocation builder refuses, before any HIP call, a shape whose
+    workspace exceeds its 8 MiB static scratch, and invalid sizes."""
+    f = lib.wise_build_support_static
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_void_p]
+    need = lib.wise_build_support_workspace_bytes(241, 512, 4)
+    assert need > 8 << 20 >= lib.wise_build_support_workspace_bytes(240, 512, 4)
+    args = (P2, 0.95, P2, P2, 1 << 40, P2, None, 0, 128, None)
+    assert f(241, 512, 4, *args) == UNSUPPORTED
+    assert f(1, 8192, 4, *args) == INVALID        # nq beyond 4096
+    assert f(0, 128, 4, *args) == INVALID
