@@ -33,8 +33,25 @@ if _ROOT not in sys.path:
     sys.path.insert(0, _ROOT)
 
 METRIC = "late-step sparse attn TFLOP/s + speedup vs dense at 4K; 32-step attn ms"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# dense bf16 MFMA work per compute unit and clock on CDNA4: four SIMDs, each
+# retiring a v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 x 2 = 32768 FLOP) every 32 cycles
+BF16_FLOP_PER_CLK_PER_CU = 4 * 32768 // 32
+HIP_DEVICE_ATTRIBUTE_CLOCK_RATE = 5   # hipDeviceAttributeClockRate (kHz), hip_runtime_api.h
+
+
+def device_peak_bf16_tflops(device_index=0):
+    """Dense bf16 MFMA peak of the device in the run: compute units x 4096 FLOP
+    per clock x the peak engine clock (hipDeviceAttributeClockRate)."""
+    import ctypes
+    import torch
+    cus = torch.cuda.get_device_properties(device_index).multi_processor_count
+    khz = ctypes.c_int(0)
+    hip = ctypes.CDLL("libamdhip64.so")
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), HIP_DEVICE_ATTRIBUTE_CLOCK_RATE, device_index) != 0:
+        raise RuntimeError("hipDeviceGetAttribute(hipDeviceAttributeClockRate) failed")
+    tflops = cus * BF16_FLOP_PER_CLK_PER_CU * khz.value * 1e3 / 1e12
+    return tflops, {"compute_units": cus, "clock_mhz": khz.value / 1e3, "flop_per_clk_per_cu": BF16_FLOP_PER_CLK_PER_CU}
 DISCOVERY_DENSE = range(1, 9)
 DISCOVERY_MASS = range(9, 13)
 REUSE = range(13, 33)
@@ -60,9 +77,9 @@ def kernel_source_digest():
 
 
 def measured_traffic(workload):
-    """HBM bytes per sparse launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None if it is missing, for another workload, or was
-    taken on a different kernel source."""
+    """Counter figures per sparse launch from the committed rocprofv3 summary
+    (FETCH_SIZE / WRITE_SIZE bytes, L2 hits and misses), or None if it is
+    missing, for another workload, or was taken on a different kernel source."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as fh:
@@ -72,7 +89,11 @@ def measured_traffic(workload):
                     kv[key] = val
         if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_digest():
             return None
-        return float(kv["hbm_bytes_per_launch"])
+        out = {"hbm_bytes": float(kv["hbm_bytes_per_launch"])}
+        for key in ("hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch", "l2_hit_rate"):
+            if key in kv:
+                out[key] = float(kv[key])
+        return out
     except (OSError, KeyError, ValueError):
         return None
 
@@ -89,9 +110,18 @@ def pairs_from_csr(row_ptr, col_idx, nq):
     return total
 
 
-def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
+def cpu_baseline(w, eta, gen_f32, budget_s=20.0, gpu_rows=None, gpu_o13=None):
     """The fp64 oracle on a bounded sample: heads 0.. of the same workload, timed
-    per stage; the late-step rate is scheduled-pair FLOP / oracle sparse time."""
+    per stage; the late-step rate is scheduled-pair FLOP / oracle sparse time.
+
+    With gpu_rows (the GPU schedule's rows, head-major) and gpu_o13 (the GPU's
+    step-13 output, [heads, n, d] on the host), the same heads also give a parity
+    sample, outside the timed stages: the GPU supports against the oracle's
+    (mismatches outside blocks within 1e-4 of the eta boundary, or within 1e-6 of
+    a mass across the cut, must be 0; the rows and blocks differing in such
+    flagged blocks are counted), and the GPU output against the oracle's sparse
+    attention over the GPU's own rows (max abs error, and the largest fraction
+    of the bf16 tolerance used)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -101,6 +131,8 @@ def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
     heads_done = 0
     t_sparse = t_dense = t_mass = t_sel = 0.0
     flops = 0
+    par = {"rows": 0, "unflagged_mismatch_rows": 0, "flagged_rows": 0, "flagged_blocks": 0,
+           "max_abs_err": 0.0, "tol_used": 0.0}
     start = time.perf_counter()
     for h in range(w.heads):
         qkv = {t: gen_f32(t, h) for t in (1, 9, 10, 11, 12, 13)}
@@ -119,6 +151,25 @@ def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
         t_sparse += t4 - t3
         flops += 4 * w.head_dim * O.scheduled_pairs(sup, w.nq)
         heads_done += 1
+        if gpu_rows is not None:
+            rows_h = gpu_rows[h * w.nq:(h + 1) * w.nq]
+            for qb in range(w.nq):
+                flagged = set()
+                for m in masses:
+                    fc, ft = O.boundary_flags(m[qb, :qb + 1], eta, 1e-4, 1e-6)
+                    flagged.update(int(b) for b in np.nonzero(fc | ft)[0])
+                diff = set(int(b) for b in rows_h[qb]) ^ set(int(b) for b in sup[qb])
+                par["rows"] += 1
+                if diff and diff <= flagged:
+                    par["flagged_rows"] += 1
+                    par["flagged_blocks"] += len(diff)
+                elif diff:
+                    par["unflagged_mismatch_rows"] += 1
+            ro, _ = O.sparse_attention(*qkv[13], rows_h)
+            err = np.abs(gpu_o13[h] - ro)
+            par["max_abs_err"] = max(par["max_abs_err"], float(err.max()))
+            # largest fraction of the bf16 tolerance 1e-2 + 2e-2 |ref| used
+            par["tol_used"] = max(par["tol_used"], float((err / (1e-2 + 2e-2 * np.abs(ro))).max()))
         if time.perf_counter() - start > budget_s:
             break
     scale = w.heads / heads_done
@@ -133,7 +184,7 @@ def cpu_baseline(w, eta, gen_f32, budget_s=20.0):
                    f"value = late-step scheduled-pair FLOP / oracle sparse time"),
         "sparse_step_ms_extrapolated": 1e3 * scale * t_sparse,
         "trajectory_ms_extrapolated": 1e3 * traj_s,
-    }
+    }, (dict(par, heads=list(range(heads_done)), step=13) if gpu_rows is not None else None)
 
 
 def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
@@ -361,6 +412,10 @@ def main():
     dense_ms = med["dense_late"] / len(REUSE)
     tflops = sparse_flop / (sparse_ms * 1e-3) / 1e12
     dense_tflops = dense_flop / (dense_ms * 1e-3) / 1e12
+    peak, peak_info = device_peak_bf16_tflops(dev.index or 0)
+    # algorithmic bytes of one sparse launch: Q, K, V read once, O written once
+    alg_bytes = 2 * w.head_dim * w.seqlen * w.batch * (2 * w.heads + 2 * w.kvh)
+    traffic = measured_traffic(w.name)
 
     result = {
         "metric": METRIC,
@@ -379,11 +434,11 @@ def main():
                    "seq_len": w.seqlen, "block": 32, "eta": eta, "recurrent_steps": 32,
                    "discovery_union_steps": [9, 12], "reuse_steps": [13, 32]},
         "late_step_tflops": round(tflops, 3),
-        "late_step_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "late_step_frac_of_peak": round(tflops / peak, 4),
         "late_step_tflops_setup_inclusive": round(len(REUSE) * sparse_flop / ((med["reuse"] + med["build"]) * 1e-3)
                                                   / 1e12, 3),
         "dense_kernel_tflops": round(dense_tflops, 3),
-        "dense_kernel_frac_of_peak": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
+        "dense_kernel_frac_of_peak": round(dense_tflops / peak, 4),
         "late_speedup_kernel_only": round(med["dense_late"] / med["reuse"], 4),
         "late_speedup_setup_inclusive": round(med["dense_late"] / (med["reuse"] + med["build"]), 4),
         "matched_full_support_late_ms": None if not m_rec else round(matched_ms, 4),
@@ -399,14 +454,19 @@ def main():
         "timed_wall_s": round(wall, 3),
         "support_diagnostics": diagnostics,
         "roofline": {
-            "kernel": "wise_sparse_attn: attn_sparse_kernel<128, 2>",
+            "kernel": f"wise_sparse_attn: attn_sparse_kernel<{w.head_dim}, 2>",
             "bound": "mfma",
             "achieved": round(tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": round(peak, 1),
+            "peak_from": dict(peak_info, formula="compute_units x flop_per_clk_per_cu x clock"),
             "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
+            "frac": round(tflops / peak, 4),
+            "traffic": None if traffic is None else traffic["hbm_bytes"],
+            "traffic_over_algorithmic": None if traffic is None else round(traffic["hbm_bytes"] / alg_bytes, 3),
+            "hbm_read_bytes": None if traffic is None else traffic.get("hbm_read_bytes_per_launch"),
+            "l2_hit_rate": None if traffic is None else traffic.get("l2_hit_rate"),
             "algorithmic_flop_per_launch": sparse_flop,
+            "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(sparse_ms, 5),
         },
     }
@@ -421,7 +481,13 @@ def main():
                 per_head[h] = Generator(w, heads=[h])
             return tuple(x[0, 0].to(torch.float64).numpy() for x in per_head[h].step_torch(t))
 
-        result["cpu_baseline"] = cpu_baseline(w, eta, gen_f32, args.cpu_budget)
+        # the GPU's step-13 output and schedule rows of the heads the oracle samples
+        o13, _ = wise.sparse_attn(*steps[13], sched)
+        torch.cuda.synchronize()
+        o13_host = o13[0].to(torch.float64).cpu().numpy()
+        gpu_rows = [ci[rp[r]:rp[r + 1]] for r in range(len(rp) - 1)]
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(w, eta, gen_f32, args.cpu_budget,
+                                                                      gpu_rows, o13_host)
     print(json.dumps(result), flush=True)
 
 

@@ -79,11 +79,15 @@ WORKLOADS = {
     "4k": Workload("4k", "bf16", 32, 128, 4096, 4, True, (0.95,), 3),
     "16k": Workload("16k", "bf16", 32, 128, 16384, 6, True, (0.90, 0.95, 0.99), 4),
     # the pages' geometries (App. B): Huginn, d = 96 with 55 heads per recurrent
-    # layer; Recurrent-Llama, grouped-query attention with 32 query / 8 key-value
-    # heads of d = 64; plus small cases of each for full parity
+    # layer and 4 recurrent layers per step; Recurrent-Llama, grouped-query
+    # attention with 32 query / 8 key-value heads of d = 64; plus small cases of
+    # each for full parity
     "d96": Workload("d96", "bf16", 5, 96, 1024, 3, True, (0.95,), 5),
     "gqa": Workload("gqa", "bf16", 8, 64, 1024, 3, True, (0.95,), 6, kv_heads=2),
     "huginn4k": Workload("huginn4k", "bf16", 55, 96, 4096, 4, True, (0.95,), 7),
+    # one Huginn recurrent step: its 4 recurrent attention layers of 55 heads in
+    # one call (independent heads, each with its own K and V)
+    "huginn4k_step": Workload("huginn4k_step", "bf16", 220, 96, 4096, 4, True, (0.95,), 9),
     "llama4k": Workload("llama4k", "bf16", 32, 64, 4096, 4, True, (0.95,), 8, kv_heads=8),
 }
 

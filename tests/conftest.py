@@ -28,3 +28,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Print the parity report the GPU tests collected: per configuration, the
+    rows compared, the rows and blocks whose GPU support differs from the
+    oracle's in boundary-flagged blocks only, and the largest output errors."""
+    try:
+        from parity_helpers import REPORT
+    except ImportError:
+        return
+    if not REPORT:
+        return
+    terminalreporter.write_sep("-", "parity report (GPU vs fp64 oracle)")
+    for cfg, fields in REPORT:
+        terminalreporter.write_line(f"{cfg}: " + ", ".join(
+            f"{k} {v:.3e}" if isinstance(v, float) else f"{k} {v}" for k, v in fields.items()))

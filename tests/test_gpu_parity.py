@@ -11,7 +11,8 @@ import torch
 import oracle as O
 from block_sparse_attention_wise_amd.synthetic import WORKLOADS, Generator
 from parity_helpers import (assert_attn_close, assert_lse_close, assert_mass_close, compare_supports,
-                            csr_rows, f64, note, oracle_union_row, schedule_from_rows, step_pair)
+                            csr_rows, f64, flagged_row_bound, note, oracle_union_row, record, schedule_from_rows,
+                            step_pair)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -98,6 +99,35 @@ def test_build_support_on_fed_masses_is_exact(name):
     assert flagged == 0
 
 
+@pytest.mark.parametrize("name,t", [("tiny", 2), ("1k", 1), ("1k", 2), ("1k", 3), ("1k", 4), ("1k", 7)])
+def test_rolling_window_supports(name, t):
+    """The rolling working set of the WISE paper (App. C.2), W^(t) = union of the
+    supports of steps max(1, t - 3) .. t: the builder over that window's masses
+    (1, 2, 3 or 4 steps) against the oracle's union over the same steps, both
+    selecting from the same fp32 masses (exact; flags at summation order only)."""
+    wise, w = _wise(), WORKLOADS[name]
+    window = tuple(range(max(1, t - 3), t + 1))
+    m32 = _oracle_masses(name, steps=window).astype(np.float32)
+    eta = w.etas[0]
+    note(f"rolling window {name} t={t} steps {window}")
+    sched = wise.build_support(torch.from_numpy(m32).to(DEV), eta, plan_head_dim=w.head_dim)
+    torch.cuda.synchronize()
+    gpu_rows = csr_rows(sched.row_ptr, sched.col_idx)
+    ref_rows, flags = [], []
+    for h in range(w.heads):
+        per_step = [O.step_supports(m32[s, h].astype(np.float64), eta) for s in range(len(window))]
+        union = O.union_supports(per_step)
+        for qb in range(w.nq):
+            _, fl = oracle_union_row([m32[s, h, qb, :qb + 1].astype(np.float64) for s in range(len(window))], eta,
+                                     cum_tol=1e-12, tie_tol=0.0)
+            ref_rows.append(union[qb])
+            flags.append(fl)
+    bad, flagged = compare_supports(gpu_rows, ref_rows, flags)
+    assert not bad, f"{len(bad)} rows differ, first {bad[:3]}"
+    assert flagged == 0
+    record(f"rolling window {name} t={t} ({len(window)} steps)", rows=len(ref_rows), flagged_blocks=flagged)
+
+
 def test_build_support_exact_ties_and_eta_edges():
     """Exact ties (dyadic masses) go to the lower block index; eta = 1 keeps all."""
     wise = _wise()
@@ -144,7 +174,12 @@ def test_sparse_attention_on_oracle_schedule(name):
 
 @pytest.mark.parametrize("name", SMALL)
 def test_end_to_end_trajectory(name):
-    """GPU masses -> GPU schedule vs the oracle's, then GPU sparse steps vs oracle."""
+    """GPU masses -> GPU schedule vs the oracle's, then GPU sparse steps vs oracle.
+
+    Supports must match the oracle's exactly outside boundary-flagged blocks, and
+    at most 1% of the rows (at least 2) may differ in flagged blocks.  Every
+    row's output is compared with the oracle's sparse attention over the GPU's
+    own schedule (for the rows whose support matches, that is the oracle's)."""
     wise, w = _wise(), WORKLOADS[name]
     eta = w.etas[0]
     g = _gen(name)
@@ -153,7 +188,7 @@ def test_end_to_end_trajectory(name):
         q, k, v = g.step_torch(t, DEV)
         note(f"e2e {name} discovery step {t}")
         wise.full_attn_mass(q, k, v, mass=mass[si])
-    sched = wise.build_support(mass, eta)
+    sched = wise.build_support(mass, eta, plan_head_dim=w.head_dim)
     torch.cuda.synchronize()
     gpu_rows = csr_rows(sched.row_ptr, sched.col_idx)
     masses = _oracle_masses(name)
@@ -163,23 +198,24 @@ def test_end_to_end_trajectory(name):
             sup, fl = oracle_union_row([masses[s, h, qb, :qb + 1] for s in range(4)], eta)
             ref_rows.append(sup)
             flags.append(fl)
-    bad, flagged = compare_supports(gpu_rows, ref_rows, flags)
-    note(f"e2e {name}: flagged mismatching blocks {flagged}")
+    flagged_rows = []
+    bad, flagged = compare_supports(gpu_rows, ref_rows, flags, flagged_rows)
+    note(f"e2e {name}: flagged mismatching rows {len(flagged_rows)}, blocks {flagged}")
     assert not bad, f"{len(bad)} rows differ outside flagged blocks, first {bad[:3]}"
-    same = [r for r in range(len(ref_rows)) if np.array_equal(gpu_rows[r], ref_rows[r])]
+    assert len(flagged_rows) <= flagged_row_bound(len(ref_rows)), f"{len(flagged_rows)} flagged rows"
     (q, k, v), dev = step_pair(g, 20)
     note(f"e2e {name} sparse step 20")
     o, lse = wise.sparse_attn(*dev, sched, want_lse=True)
     torch.cuda.synchronize()
+    worst_abs = worst_tol = 0.0
     for h in range(w.heads):
         ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h // w.group]), f64(v[0, h // w.group]),
-                                    ref_rows[h * w.nq:(h + 1) * w.nq])
-        keep = np.zeros(w.seqlen, dtype=bool)
-        for r in same:
-            if r // w.nq == h:
-                keep[(r % w.nq) * 32:(r % w.nq + 1) * 32] = True
-        assert_attn_close(f64(o[0, h])[keep], ro[keep], w.dtype, f"{name} head {h} O")
-        assert_lse_close(f64(lse[0, h])[keep], rl[keep], w.dtype, f"{name} head {h}")
+                                    gpu_rows[h * w.nq:(h + 1) * w.nq])
+        ea, er = assert_attn_close(f64(o[0, h]), ro, w.dtype, f"{name} head {h} O")
+        assert_lse_close(f64(lse[0, h]), rl, w.dtype, f"{name} head {h}")
+        worst_abs, worst_tol = max(worst_abs, ea), max(worst_tol, er)
+    record(f"trajectory {name} (eta {eta}, step 20, all rows)", rows=len(ref_rows),
+           flagged_rows=len(flagged_rows), flagged_blocks=flagged, max_abs=worst_abs, tol_used=worst_tol)
 
 
 @pytest.mark.parametrize("name", ["tiny", "1k"])
@@ -454,3 +490,51 @@ def test_execution_plan_lists_each_union_block_once(bh, nq, eta, hd):
                 keep[32 * qb:32 * qb + 32] = True
         assert_attn_close(f64(op[0, h])[keep], ro[keep], "bf16", f"plan head {h} O")
         assert_lse_close(f64(lp[0, h])[keep], rl[keep], "bf16", f"plan head {h}")
+
+
+def test_high_dynamic_range_logits():
+    """Logits spread over more than 60 (natural-log units) and a dominant key
+    whose logit lifts the running maximum by tens of units in the middle of the
+    rows: dense attention, both block-mass epilogues and sparse attention through
+    the execution plan against the oracle (the GPU counterpart of the oracle's
+    dominant-key pin)."""
+    wise = _wise()
+    rng = np.random.default_rng(77)
+    n, d, heads, nq = 1024, 128, 2, 32
+    s = np.sqrt(20.0)                       # q.k / sqrt(d) has standard deviation s^2 = 20
+    q = rng.standard_normal((1, heads, n, d)) * s
+    k = rng.standard_normal((1, heads, n, d)) * s
+    v = rng.standard_normal((1, heads, n, d))
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q[:, :, 480:] += 40.0 * u               # queries 480.. share a direction ...
+    k[:, :, 500] += 40.0 * u                # ... that key 500 carries: about +140 for rows >= 500
+    q, k, v = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16) for x in (q, k, v))
+    dq, dk, dv = q.to(DEV), k.to(DEV), v.to(DEV)
+    note("high dynamic range: dense, masses, sparse")
+    o, lse = wise.dense_attn(dq, dk, dv, want_lse=True)
+    _, _, m1 = wise.full_attn_mass(dq, dk, dv, want_mass=True)
+    _, _, m2 = wise.full_attn_mass(dq, dk, dv, want_mass=True, workspace=False)
+    sched = wise.build_support(m1.unsqueeze(0).contiguous(), 0.95, plan_head_dim=d)
+    os_, ls_ = wise.sparse_attn(dq, dk, dv, sched, want_lse=True)
+    torch.cuda.synchronize()
+    rows = csr_rows(sched.row_ptr, sched.col_idx)
+    worst = [0.0, 0.0]
+    for h in range(heads):
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        logits = (qh @ kh.T) / np.sqrt(d)
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        span = logits[causal].max() - logits[causal].min()
+        assert span > 60 and logits[600, 500] - np.delete(logits[600, :601], 500).max() > 20
+        ro, rl = O.causal_attention(qh, kh, vh)
+        ea, er = assert_attn_close(f64(o[0, h]), ro, "bf16", f"hdr dense head {h} O")
+        assert_lse_close(f64(lse[0, h]), rl, "bf16", f"hdr dense head {h}")
+        rm = O.block_mass(qh, kh)
+        assert_mass_close(f64(m1[h]), rm, "bf16", f"hdr one-pass mass head {h}")
+        assert_mass_close(f64(m2[h]), rm, "bf16", f"hdr sweep mass head {h}")
+        so, sl = O.sparse_attention(qh, kh, vh, rows[h * nq:(h + 1) * nq])
+        es, rs = assert_attn_close(f64(os_[0, h]), so, "bf16", f"hdr sparse head {h} O")
+        assert_lse_close(f64(ls_[0, h]), sl, "bf16", f"hdr sparse head {h}")
+        worst = [max(worst[0], ea, es), max(worst[1], er, rs)]
+    record("high dynamic range (logit span > 60, dominant key)", rows=heads * nq, max_abs=worst[0],
+           tol_used=worst[1])
