@@ -539,18 +539,26 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // Consecutive workgroups land on consecutive XCDs (p mod 8).  XCD x works on
   // one contiguous run of heads, x * bhn/8 .. (x+1) * bhn/8 - 1 (the first bhn
   // mod 8 runs one head longer), so the query heads of one key-value group share
-  // that XCD's L2; its k-th workgroup (k = p / 8) takes the (k / run)-th longest
-  // query group of head k mod run of its run: longest first over all heads.
-  // The grid has 8 * ceil(bhn / 8) * per_head workgroups; those past an XCD's
-  // run hold no work.
+  // that XCD's L2.  It takes its run hg heads at a time, hg the fewest heads
+  // whose groups fill the XCD's resident workgroup slots twice over: enough
+  // groups in flight to balance the longest against the shortest, and no more
+  // heads' K and V competing for the XCD's 4 MB L2 than that needs.  Within a
+  // chunk of hc heads its k-th workgroup (k = p / 8, counted from the chunk's
+  // first) takes the (k / hc)-th longest query group of the chunk's head k mod
+  // hc: longest first over the chunk.  The grid has 8 * ceil(bhn / 8) *
+  // per_head workgroups; those past an XCD's run hold no work.
   int bh, rank;
   {
+    constexpr int kSlotsPerXcd = 32 * (4 * stream_occupancy<D, MODE>() / W);  // 32 CUs, 4 SIMDs each
     const int x = (int)(blockIdx.x & 7u), k = (int)(blockIdx.x >> 3);
     const int base = bhn >> 3, rem = bhn & 7;
     const int run = base + (x < rem ? 1 : 0), start = x * base + min(x, rem);
     if (k >= run * per_head) return;  // uniform over the workgroup
-    bh = start + k % run;
-    rank = k / run;
+    const int hg = min(run, max(1, (2 * kSlotsPerXcd + per_head - 1) / per_head));
+    const int c = k / (hg * per_head), within = k - c * hg * per_head;
+    const int hc = min(hg, run - c * hg);  // the last chunk may hold fewer heads
+    bh = start + c * hg + within % hc;
+    rank = within / hc;
   }
   int qb, qlast, pgroup = 0;
   if (use_plan) {
