@@ -221,8 +221,7 @@ def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
                     "retained_future_mass": {f"t{t}": retained(sched, t) for t in (13, 20, 32)}}}
     for kind in ("static", "size_matched", "mass_matched"):
         ctl = wise.alloc_schedule(bh, nq, mass.device)
-        build = lambda: wise.build_support_variant(kind, m1, eta=eta, reference=sched, schedule=ctl, workspace=ws,
-                                                   plan_head_dim=w.head_dim)
+        build = lambda: wise.build_support_variant(kind, m1, eta=eta, reference=sched, schedule=ctl, workspace=ws)
         build_ms = timed(build)
         sparse_ms = timed(lambda: wise.sparse_attn(*steps[32], ctl, out=out))
         res[{"static": "static95"}.get(kind, kind)] = {
@@ -234,8 +233,7 @@ def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
             blk = wise.alloc_schedule(bh, nq, mass.device)
             wsb = torch.empty(int(wise.lib.wise_build_support_blocked_workspace_bytes(bh, nq, 4, block)),
                               dtype=torch.uint8, device=mass.device)
-            build_ms = timed(lambda: wise.build_support(mass, eta, schedule=blk, workspace=wsb, block=block,
-                                                        plan_head_dim=w.head_dim))
+            build_ms = timed(lambda: wise.build_support(mass, eta, schedule=blk, workspace=wsb, block=block))
             sparse_ms = timed(lambda: wise.sparse_attn(*steps[32], blk, out=out))
             res[f"block{block}"] = {
                 "block_density": round(int(blk.nnz.item()) / causal, 5),
@@ -311,7 +309,7 @@ def main():
     ws = torch.empty(wise.build_support_workspace_bytes(bh, nq, 4), dtype=torch.uint8, device=dev)
     full_sched = wise.alloc_schedule(bh, nq, dev)
     wise.build_support(torch.ones((1, bh, nq, nq), dtype=torch.float32, device=dev), 1.0,
-                       schedule=full_sched, workspace=ws, plan_head_dim=w.head_dim)
+                       schedule=full_sched, workspace=ws)
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -324,7 +322,7 @@ def main():
         for si, t in enumerate(DISCOVERY_MASS):
             wise.full_attn_mass(*steps[t], out=out, mass=mass[si])
         e[2].record(stream)
-        wise.build_support(mass, eta, schedule=sched, workspace=ws, plan_head_dim=w.head_dim)
+        wise.build_support(mass, eta, schedule=sched, workspace=ws)
         e[3].record(stream)
         for t in REUSE:
             wise.sparse_attn(*steps[t], sched, out=out)
@@ -454,7 +452,7 @@ def main():
         "timed_wall_s": round(wall, 3),
         "support_diagnostics": diagnostics,
         "roofline": {
-            "kernel": f"wise_sparse_attn: attn_sparse_kernel<{w.head_dim}, 2>",
+            "kernel": f"wise_sparse_attn: attn_rows_kernel<{w.head_dim}>",
             "bound": "mfma",
             "achieved": round(tflops, 3),
             "peak": round(peak, 1),

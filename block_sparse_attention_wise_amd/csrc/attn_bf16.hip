@@ -27,6 +27,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace wise {
 
 template <int D>
@@ -155,6 +157,37 @@ struct QRegs {
   __device__ __forceinline__ bf16x8 get(int c) const { return f[c]; }
 };
 
+// K/V operands read from N pairs of LDS tiles (kt[n], vt[n]) as they are used.
+template <int D, int N>
+struct LdsKV {
+  const __bf16* kt[N];
+  const __bf16* vt[N];
+  const KOps& kops;
+  const VOps& vops;
+  __device__ __forceinline__ bf16x8 k(int n, int c) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kt[n]) + kops.ko[c & 1] +
+                                            tile_offset(0, 4 * (c >> 1)));
+  }
+  __device__ __forceinline__ bf16x8 v(int n, int t, int c2) const { return v_operand<D>(vt[n], vops, t, c2); }
+};
+// K/V operands of one block, read from its LDS tiles into registers up front.
+template <int D>
+struct RegKV {
+  bf16x8 kf[Tile<D>::NC];
+  bf16x8 vf[Tile<D>::NT][2];
+  __device__ __forceinline__ void load(const __bf16* kt, const __bf16* vt, const KOps& kops, const VOps& vops) {
+    const LdsKV<D, 1> src{{kt}, {vt}, kops, vops};
+#pragma unroll
+    for (int c = 0; c < Tile<D>::NC; ++c) kf[c] = src.k(0, c);
+#pragma unroll
+    for (int t = 0; t < Tile<D>::NT; ++t)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) vf[t][c2] = src.v(0, t, c2);
+  }
+  __device__ __forceinline__ bf16x8 k(int, int c) const { return kf[c]; }
+  __device__ __forceinline__ bf16x8 v(int, int t, int c2) const { return vf[t][c2]; }
+};
+
 template <int D, class QS>
 __device__ __forceinline__ floatx16 qk_tile(const bf16x8 (&kf)[Tile<D>::NC], const QS& q) {
   floatx16 s = {};
@@ -219,11 +252,12 @@ __device__ __forceinline__ float max_tree3(const float (&v)[K]) {
 // log-sum-exps of its scaled logits over keys 0..15 and 16..31 (log2 units) are
 // stored at blse + bidx[n] * 64 + {0, 32} + query, where the block-mass epilogue
 // reads them back.
-template <int D, int N, class QS, bool SUB = false, int BL = 0>
-__device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* const (&kt)[N], const QS& qf,
-                                             const __bf16* const (&vt)[N], const bool (&diag)[N], int i, int h,
-                                             const KOps& kops, const VOps& vops, float sl2, int sub_bits,
-                                             float* blse, const int* bidx) {
+// The K and V^T operands come from kv: kv.k(n, c) is the K fragment of block n
+// for MFMA step c, kv.v(n, t, c2) the V^T operand of output tile t and key
+// chunk c2 (LdsKV reads them from the LDS tiles, RegKV holds them).
+template <int D, int N, class QS, class KV, bool SUB = false, int BL = 0>
+__device__ __forceinline__ void attend_tiles(RowState<D>& st, const KV& kv, const QS& qf, const bool (&diag)[N],
+                                             int i, int h, float sl2, int sub_bits, float* blse, const int* bidx) {
   using T = Tile<D>;
   floatx16 s[N];
 #pragma unroll
@@ -234,11 +268,7 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
 #pragma unroll
   for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kt[n]) + kops.ko[c & 1] +
-                                                          tile_offset(0, 4 * (c >> 1)));
-      s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf.get(c), s[n], 0, 0, 0);
-    }
+    for (int n = 0; n < N; ++n) s[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv.k(n, c), qf.get(c), s[n], 0, 0, 0);
   }
   __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -319,8 +349,7 @@ __device__ __forceinline__ void attend_tiles(RowState<D>& st, const __bf16* cons
     for (int t = 0; t < T::NT; ++t)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
-        st.acc[t] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt[n], vops, t, c2), pb[c2], st.acc[t], 0, 0, 0);
+        st.acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv.v(n, t, c2), pb[c2], st.acc[t], 0, 0, 0);
   }
   st.l += lsum;
 }
@@ -367,7 +396,7 @@ __device__ __forceinline__ float finish_rows(const RowState<D>& st, __bf16* orow
 // trip ahead of the compute through register staging sets.
 
 constexpr int kWaves = 4;       // four-row workgroups
-constexpr int kSparseWaves = kPlanRows;  // sparse workgroups
+constexpr int kSparseWaves = 4;  // 16-token sparse workgroups
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with expcnt/lgkmcnt left free
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 constexpr int kMaxMaskWords = 128;  // sparse rows: nq <= 4096
@@ -376,7 +405,7 @@ constexpr int kEntryShift = 8;      // list entries: (block << 8) | row mask
 
 // kDenseMass16 / kSparse16: the block mass and the schedule at 16-token blocks
 enum StreamMode { kDense = 0, kDenseMass = 1, kSparse = 2, kDenseMass16 = 3, kSparse16 = 4 };
-constexpr int kSparseTrip = kPlanTrip;  // tiles per trip of the sparse kernel
+constexpr int kSparseTrip = 2;  // tiles per trip of the 16-token sparse mode
 
 // Wavefronts per SIMD (two, up to 256 VGPRs each: the two-block softmax steps,
 // and the sparse modes' four staging sets, need the registers), three where a
@@ -453,44 +482,6 @@ struct UnionList {
     return c[0] >= 0;
   }
 };
-// a precomputed execution plan (wise_build_support): the group's entries in
-// trip order, 64 per chunk, one per lane, read with readlane; the next chunk is
-// loaded while the current one is read.  Entries naming a block past the
-// group's last query block, or with no row, become holes (-1).
-struct PlanList {
-  const int32_t* e;
-  int base, end, qlast, lane;
-  int cur, nxt;  // entries base .. base + 63 and the 64 after them
-  int idx;       // next entry within the current chunk
-  __device__ __forceinline__ int load(int at) const { return at + lane < end ? e[at + lane] : -1; }
-  __device__ __forceinline__ void start(int first, int count) {
-    base = first;
-    end = first + count;
-    idx = 0;
-    cur = load(base);
-    nxt = load(base + 64);
-  }
-  __device__ __forceinline__ int entry(int at) const {
-    const int v = base + at < end ? __builtin_amdgcn_readlane(cur, at) : -1;
-    return v >= 0 && (v >> kEntryShift) <= qlast && (v & 0xFF) != 0 ? v : -1;
-  }
-  template <int T>
-  __device__ __forceinline__ bool next_trip(int (&c)[T]) {
-    static_assert(64 % T == 0, "trips do not straddle chunks");
-    if (base + idx >= end) return false;
-    if (idx == 64) {
-      base += 64;
-      idx = 0;
-      cur = nxt;
-      nxt = load(base + 64);
-    }
-#pragma unroll
-    for (int u = 0; u < T; ++u) c[u] = entry(idx + u);
-    idx += T;
-    return true;
-  }
-};
-
 template <int D, int MODE>
 __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   using T = Tile<D>;
@@ -533,9 +524,7 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   vops.init(lane);
   const int ngroups = (a.nq + W - 1) / W;
   const int bhn = a.rows / a.nq;
-  constexpr bool PLAN_ROWS = SPARSE && !SUB;  // rows may come from an execution plan
-  const bool use_plan = PLAN_ROWS && a.plan != nullptr;
-  const int per_head = use_plan ? plan_groups_per_head(a.nq) : ngroups;  // query groups per head
+  const int per_head = ngroups;  // query groups per head
   // Consecutive workgroups land on consecutive XCDs (p mod 8).  XCD x works on
   // one contiguous run of heads, x * bhn/8 .. (x+1) * bhn/8 - 1 (the first bhn
   // mod 8 runs one head longer), so the query heads of one key-value group share
@@ -560,28 +549,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
     bh = start + c * hg + within % hc;
     rank = within / hc;
   }
-  int qb, qlast, pgroup = 0;
-  if (use_plan) {
-    // the plan's groups of this head come longest first; rank-th group; its
-    // rows are listed first, -1 after (rows outside 0..nq-1 are ignored)
-    const int gh = per_head;
-    pgroup = bh * gh + rank;
-    const int32_t* gr = a.plan + bhn * gh + 1 + (size_t)kPlanRows * pgroup;
-    qb = -1;
-    qlast = -1;
-#pragma unroll
-    for (int w = 0; w < kPlanRows; ++w) {
-      int r = gr[w];
-      r = r >= 0 && r < a.nq ? r : -1;
-      if (w == wave) qb = r;
-      qlast = max(qlast, r);
-    }
-    if (qlast < 0) return;  // an empty group (uniform over the workgroup)
-  } else {
-    const int grp = ngroups - 1 - rank;
-    qb = W * grp + wave;
-    qlast = min(W * grp + W, a.nq) - 1;
-  }
+  const int grp = ngroups - 1 - rank;
+  const int qb = W * grp + wave;
+  const int qlast = min(W * grp + W, a.nq) - 1;
   const bool active = qb >= 0 && qb < a.nq;
   const size_t head_off = (size_t)bh * a.seqlen * D;
   // grouped-query attention: query head h of batch b reads key-value head
@@ -596,19 +566,9 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
   // (keeping the in-loop waits on the prefetched K/V tiles only).
   QRegs<D> qf;
   load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * (active ? qb : qlast) + i) * D, h);
-  // sparse mode with an execution plan: group g's entry count plan[g] and its
-  // first entries (fixed slot of nq entries) load together with Q
-  PlanList plist{nullptr, 0, 0, qlast, lane, -1, -1, 0};
-  if (use_plan) {
-    const int groups = bhn * plan_groups_per_head(a.nq), g = pgroup;
-    const int slot = g * a.nq;  // plan capacity (checked on the host) covers every slot
-    plist.e = a.plan + groups + 1 + kPlanRows * groups;
-    const int cnt = a.plan[g];
-    plist.start(slot, cnt < 0 ? 0 : (cnt > a.nq ? a.nq : cnt));
-  }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-  if (SPARSE && (a.plan == nullptr || SUB)) {
+  if (SPARSE) {
     // this wavefront's row as a bitmask over key blocks (entries outside 0..qb
     // and offsets outside 0..col_cap are ignored; duplicates count once)
     const int nwords = (qlast >> 5) + 1;
@@ -762,27 +722,23 @@ __device__ __forceinline__ void attn_stream(const AttnBf16Args& a) {
       mine &= mine - 1;
       const int u1 = __builtin_ctz(mine);
       mine &= mine - 1;
-      const __bf16* const kp[2] = {kb + u0 * KE, kb + u1 * KE};
-      const __bf16* const vp[2] = {vb + u0 * VE, vb + u1 * VE};
+      const LdsKV<D, 2> kv{{kb + u0 * KE, kb + u1 * KE}, {vb + u0 * VE, vb + u1 * VE}, kops, vops};
       const bool dp[2] = {((dg >> u0) & 1) != 0, ((dg >> u1) & 1) != 0};
       const int bi[2] = {c[u0] >> kEntryShift, c[u1] >> kEntryShift};
-      attend_tiles<D, 2, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, kops, vops, a.scale_log2,
-                                            sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi);
+      attend_tiles<D, 2, QRegs<D>, LdsKV<D, 2>, SUB, BL>(st, kv, qf, dp, i, h, a.scale_log2,
+                                                         sub4(bi[0]) | (sub4(bi[1]) << 4), blse, bi);
     }
     while (mine) {
       const int u0 = __builtin_ctz(mine);
       mine &= mine - 1;
-      const __bf16* const kp[1] = {kb + u0 * KE};
-      const __bf16* const vp[1] = {vb + u0 * VE};
+      const LdsKV<D, 1> kv{{kb + u0 * KE}, {vb + u0 * VE}, kops, vops};
       const bool dp[1] = {((dg >> u0) & 1) != 0};
       const int bi[1] = {c[u0] >> kEntryShift};
-      attend_tiles<D, 1, QRegs<D>, SUB, BL>(st, kp, qf, vp, dp, i, h, kops, vops, a.scale_log2, sub4(bi[0]) | 0xF0,
-                                            blse, bi);
+      attend_tiles<D, 1, QRegs<D>, LdsKV<D, 1>, SUB, BL>(st, kv, qf, dp, i, h, a.scale_log2, sub4(bi[0]) | 0xF0,
+                                                         blse, bi);
     }
   };
-  if (use_plan) {
-    stream(plist, attend);
-  } else if (SPARSE) {
+  if (SPARSE) {
     UnionList<W, MW> list{rmask, (qlast >> 5) + 1, 0, 0u};
     list.u = list.word_union(0);
     stream(list, attend);
@@ -984,13 +940,196 @@ __global__ __launch_bounds__(64 * kSparseWaves) __attribute__((
   attn_stream<D, MODE>(a);
 }
 
+// ------------------------------------------------------------------ row-stream sparse kernel
+//
+// Block-sparse attention at 32-token blocks.  A reuse-step row's scheduled key
+// blocks are mostly its own (the selected blocks of neighbouring query blocks
+// overlap little: at 4k, four-row groups would use 39% of their wavefront
+// steps), so a workgroup is one wavefront owning one query block.  It streams
+// its row's blocks through one LDS slot of its own, with no barrier and no
+// idle wavefront: at the start of a step the block's K and V operands move from
+// the slot to registers, the slot refills with the next block, and the block
+// is computed from the registers while that copy runs.  Two such wavefronts
+// share each SIMD, so one's copy waits, row set-up and output stores overlap
+// the other's matrix work.
+//
+// The row's blocks are walked in ascending order from a bitmask over key blocks
+// held in two VGPRs (word w in lane w % 64 of register w / 64), built from the
+// CSR row: entries outside 0..qb are ignored and duplicates count once.
+
+// LDS bytes of one row-stream workgroup: one slot of a K and a V tile.
+template <int D>
+constexpr int rows_lds_bytes() {
+  return 2 * Tile<D>::BYTES;
+}
+// Row-stream workgroups resident per CU: two wavefronts per SIMD, within the
+// 160 KiB of LDS.
+template <int D>
+constexpr int rows_per_cu() {
+  return (160 * 1024) / rows_lds_bytes<D>() < 8 ? (160 * 1024) / rows_lds_bytes<D>() : 8;
+}
+
+// Ascending walk over the set bits of a row bitmask of nw words.
+struct MaskWalk {
+  uint32_t w0, w1;  // words lane and 64 + lane
+  int w, nw;        // current word (wave-uniform), word count
+  uint32_t cur;     // unvisited bits of the current word
+  __device__ __forceinline__ uint32_t word(int x) const {
+    return (uint32_t)__builtin_amdgcn_readlane((int)(x < 64 ? w0 : w1), x & 63);
+  }
+  __device__ __forceinline__ int next() {
+    while (cur == 0u) {
+      if (++w >= nw) return -1;
+      cur = word(w);
+    }
+    const int b = 32 * w + __builtin_ctz(cur);
+    cur &= cur - 1u;
+    return b;
+  }
+};
+
+// s_waitcnt vmcnt(N) that the compiler does not move memory accesses across
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// every LDS read issued so far has returned (before a copy refills its slot)
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_rows_kernel(AttnBf16Args a) {
+  using T = Tile<D>;
+  constexpr int CI = D / 16;  // wave-copies per tile
+  __shared__ __attribute__((aligned(1024))) unsigned char slot[2 * T::BYTES];  // K tile, then V tile
+  static_assert(sizeof(slot) == rows_lds_bytes<D>(), "LDS budget");
+
+  const int lane = threadIdx.x;
+  const int i = lane & 31, h = lane >> 5;
+  const int bhn = a.rows / a.nq;
+  // rank r of a head: its r-th row in the schedule's row order (longest first),
+  // or query block nq - 1 - r without one (later rows tend to be longer)
+  const int per_head = a.nq;
+  // XCD-aligned head runs taken hg heads at a time, as in the streaming kernel,
+  // hg the fewest heads whose rows fill the XCD's workgroup slots twice over: a
+  // row is one wavefront's serial work, so the longest rows of all the heads in
+  // flight have to start in the first rounds of slots; a larger hg would only
+  // spread the XCD's L2 over more heads' K and V
+  int bh, rank;
+  {
+    constexpr int kSlotsPerXcd = 32 * rows_per_cu<D>();
+    const int x = (int)(blockIdx.x & 7u), k = (int)(blockIdx.x >> 3);
+    const int base = bhn >> 3, rem = bhn & 7;
+    const int run = base + (x < rem ? 1 : 0), start = x * base + min(x, rem);
+    if (k >= run * per_head) return;
+    const int hg = min(run, max(1, (2 * kSlotsPerXcd + per_head - 1) / per_head));
+    const int c = k / (hg * per_head), within = k - c * hg * per_head;
+    const int hc = min(hg, run - c * hg);
+    bh = start + c * hg + within % hc;
+    rank = within / hc;
+  }
+  int qb;
+  if (a.plan != nullptr) {
+    qb = a.plan[(size_t)bh * a.nq + rank];
+    if (qb < 0 || qb >= a.nq) return;  // not a row (a row order from the builder has none)
+  } else {
+    qb = a.nq - 1 - rank;
+  }
+  const size_t head_off = (size_t)bh * a.seqlen * D;
+  const int bb = bh / a.heads, hq = bh - bb * a.heads;
+  const size_t kv_off = (size_t)(bb * (a.heads / a.kv_group) + hq / a.kv_group) * a.seqlen * D;
+  const uint32_t kv_bytes = (uint32_t)a.seqlen * (uint32_t)(D * 2);
+  const u32x4 rsk = buffer_resource(a.k + kv_off, kv_bytes), rsv = buffer_resource(a.v + kv_off, kv_bytes);
+
+  QRegs<D> qf;
+  load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * qb + i) * D, h);
+
+  // the row's bitmask
+  MaskWalk walk{0u, 0u, 0, (qb >> 5) + 1, 0u};
+  {
+    const int row = bh * a.nq + qb;
+    int64_t e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
+    e0 = e0 < 0 ? 0 : (e0 > a.col_cap ? a.col_cap : e0);
+    e1 = e1 < e0 ? e0 : (e1 > a.col_cap ? a.col_cap : e1);
+    for (int64_t base = e0; base < e1; base += 64) {
+      int b = base + lane < e1 ? a.col_idx[base + lane] : -1;
+      b = b >= 0 && b <= qb ? b : -1;
+      uint64_t todo = __ballot(b >= 0);
+      while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int bj = __builtin_amdgcn_readlane(b, j);
+        const int w = bj >> 5;
+        if ((w & 63) == lane) {
+          if (w < 64)
+            walk.w0 |= 1u << (bj & 31);
+          else
+            walk.w1 |= 1u << (bj & 31);
+        }
+      }
+    }
+    walk.cur = walk.word(0);
+  }
+
+  // Copy x of a tile fills block x of its LDS layout (tile_offset): lane j
+  // fetches row 16 (x % 2) + j / 4, chunk 4 (x / 2) + ((j % 4) ^ (j / 16 % 4)).
+  const uint32_t lane_src = (uint32_t)((lane >> 2) * (2 * D) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const uint32_t lb = lds_address(slot);
+  auto issue = [&](int b) {
+    const uint32_t tile = (uint32_t)b * (uint32_t)T::BYTES;
+#pragma unroll
+    for (int x = 0; x < CI; ++x)
+      copy_to_lds(rsk, lb + 1024 * x, lane_src, tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64));
+#pragma unroll
+    for (int x = 0; x < CI; ++x)
+      copy_to_lds(rsv, lb + T::BYTES + 1024 * x, lane_src, tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64));
+  };
+  KOps kops;
+  kops.init(i, h);
+  VOps vops;
+  vops.init(lane);
+  RowState<D> st;
+  st.init();
+  int c = walk.next();  // this step's block
+  if (c >= 0) issue(c);
+  // Q (loaded before the copies) and the first block in place.  Q then passes
+  // through an empty asm statement, so that the compiler, which does not count
+  // the copies, sees no load of Q outstanding in the loop and adds no vmcnt
+  // wait there (one would also wait for the copy in flight).
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+  for (int x = 0; x < T::NC; ++x) asm volatile("" : "+v"(qf.f[x]));
+  while (c >= 0) {
+    RegKV<D> kv;
+    kv.load(reinterpret_cast<const __bf16*>(slot), reinterpret_cast<const __bf16*>(slot + T::BYTES), kops, vops);
+    lds_reads_done();
+    const int next = walk.next();
+    if (next >= 0) issue(next);
+    const bool dp[1] = {c == qb};
+    const int bi[1] = {c};
+    attend_tiles<D, 1, QRegs<D>, RegKV<D>, false, 0>(st, kv, qf, dp, i, h, a.scale_log2, 0xFF, nullptr, bi);
+    c = next;
+    if (c >= 0) wait_vm<0>();  // its copy has landed
+  }
+
+  float* lse_out = a.lse != nullptr ? a.lse + (size_t)bh * a.seqlen + 32 * qb + i : nullptr;
+  finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
+}
+
+template <int D>
+static void launch_rows(const AttnBf16Args& a, hipStream_t stream) {
+  const int bhn = a.rows / a.nq;
+  const dim3 grid(8 * ((bhn + 7) / 8) * a.nq), block(64);
+  hipLaunchKernelGGL((attn_rows_kernel<D>), grid, block, 0, stream, a);
+}
+
 // ------------------------------------------------------------------ launch
 
 template <int D, int MODE>
 static void launch_mode(const AttnBf16Args& a, hipStream_t stream) {
   constexpr int w = stream_waves<D, MODE>();
   const int bhn = a.rows / a.nq;
-  const int per_head = MODE == kSparse && a.plan != nullptr ? plan_groups_per_head(a.nq) : (a.nq + w - 1) / w;
+  const int per_head = (a.nq + w - 1) / w;
   const dim3 grid(8 * ((bhn + 7) / 8) * per_head), block(64 * w);  // XCD-aligned head runs
   if constexpr (MODE == kSparse || MODE == kSparse16)
     hipLaunchKernelGGL((attn_sparse_kernel<D, MODE>), grid, block, 0, stream, a);
@@ -1004,7 +1143,7 @@ static void launch_d(const AttnBf16Args& a, bool sparse, bool mass, bool b16, hi
     if (b16)
       launch_mode<D, kSparse16>(a, stream);
     else
-      launch_mode<D, kSparse>(a, stream);
+      launch_rows<D>(a, stream);
   } else if (mass) {
     if (b16)
       launch_mode<D, kDenseMass16>(a, stream);

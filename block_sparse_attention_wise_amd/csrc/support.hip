@@ -24,9 +24,8 @@
 //                 nnz.
 //   emit_csr      one wavefront per row: expands the bitmask into ascending
 //                 col_idx entries at row_ptr[row].
-//   group_rows    one workgroup per head: groups the head's rows for the sparse
-//                 kernel (execution plan).
-//   group_plan    one wavefront per group: the group's union tiles in trips.
+//   order_rows    one workgroup per head: the head's query blocks, longest
+//                 scheduled row first (the sparse kernel's launch order).
 #include "common.h"
 #include "kernels.h"
 
@@ -316,81 +315,35 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
   }
 }
 
-// ---------------------------------------------------------------- execution plan
+// ---------------------------------------------------------------- row order
 //
-// Groups of up to kPlanRows query blocks (rows) of one head are the sparse
-// kernel's work units.  A group's plan lists the union of its rows' key blocks,
-// each entry (block << 8) | membership mask (bit w: the group's row w schedules it),
-// ordered in trips of kPlanTrip tiles (the tiles the kernel holds in LDS at
-// once, between two barriers) so that the rows' blocks spread evenly over the
-// trips: a trip lasts as long as its busiest row, so each trip is filled
-// greedily with the tiles that raise its busiest row the least.  The order of a
-// row's blocks only changes the floating-point summation order of its softmax.
-
-static_assert(kPlanRows >= 1 && kPlanRows <= 8, "plan rows fit the 8-bit membership mask");
-static_assert(kPlanTrip >= 1 && kPlanTrip <= 16, "plan trip");
-constexpr int kMasks = 1 << kPlanRows;
-
-// Which rows share a group.  A group's workgroup runs one trip per kPlanTrip
-// tiles of its rows' union, and each trip lasts as long as its busiest row, so a
-// group of u union tiles whose longest row has m tiles costs about
-// kTripCost * ceil(u / kPlanTrip) + kTileCost * m: the per-trip loads, stores
-// and barriers against one softmax step per tile of the busiest row (weights in
-// the proportion measured for the 4k late step, 1.85 and 0.80 us).  Rows of
-// similar length waste the least time at the trip barriers, so each head's rows
-// are taken longest first (ties: lower index first) and packed greedily, up to
-// kPlanRows per group.  A group is closed early when the next row would push its
-// cost above a cap, a fraction of the cost of the longest row of the whole
-// schedule on its own: the kernel cannot end before that row's group does, and
-// much longer groups would only lengthen the tail.  Measured on the 4k, Huginn
-// and Llama geometries, 5/4 is best at head_dim 128 and 96 (lower caps split
-// too many groups), 9/10 at 64, where three workgroups share a CU and the
-// longest groups decide the kernel's end.  A head has at most
-// plan_groups_per_head(nq) groups: once
-// the rows left would not fit in the groups left, groups are only closed when
-// full.  Groups come out longest first, the order the sparse kernel launches
-// them in; unused groups list no rows (-1).
-constexpr int kTripCost = 9, kTileCost = 4;
-constexpr int kGroupThreads = 256;
-constexpr int kGroupChunk = 64;  // rows whose bitmasks are staged in LDS at once
+// The sparse kernel gives each query block (row) one wavefront that works
+// through the row's key blocks on its own, so a row's scheduled length is its
+// wavefront's serial work and the kernel ends after its longest rows do.  The
+// schedule's row order lists each head's query blocks by scheduled length,
+// longest first (ties: lower index first); the kernel starts rows in that order
+// so that the longest ones start first.  It only changes which rows run when.
+constexpr int kOrderThreads = 256;
 constexpr int kRankSortMax = 1024;  // rows sorted by rank (else bitonic)
-static_assert(kMaxNq <= 4096 && kMaxNq / 32 <= 128, "sort key and two union words per lane");
+static_assert(kMaxNq <= 4096, "12-bit row index in the sort key");
 
-__device__ __forceinline__ int group_cost(int u, int m) {
-  return kTripCost * ((u + kPlanTrip - 1) / kPlanTrip) + kTileCost * m;
-}
-
-// sum over the wavefront, in lane 63 (DPP row shifts, then row broadcasts)
-__device__ __forceinline__ int wave_sum_dpp(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return __builtin_amdgcn_readlane(x, 63);
-}
-
-__global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_t* masks, const int32_t* counts,
-                                                                   const int32_t* max_count, int nq, int nwords,
-                                                                   int gh, int cap_num, int cap_den, int32_t* rows) {
+__global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(const int32_t* counts, int nq, int32_t* order) {
   __shared__ uint32_t keys[kMaxNq];
-  __shared__ uint32_t stage[kGroupChunk * (kMaxNq / 32)];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint32_t sorted[kRankSortMax];
+  const int h = blockIdx.x, tid = threadIdx.x;
   const int32_t* cnt = counts + (size_t)h * nq;
   // sort keys (count descending, row ascending; all distinct): up to
   // kRankSortMax rows each key goes to its rank, the number of smaller keys
   // (broadcast LDS reads, no barrier per pass); beyond, bitonic over a power of two
   int n2 = 1;
   while (n2 < nq) n2 <<= 1;
-  for (int q = tid; q < n2; q += kGroupThreads) {
+  for (int q = tid; q < n2; q += kOrderThreads) {
     const int c = q < nq ? min(max(cnt[q], 0), nq) : 0;
     keys[q] = q < nq ? ((uint32_t)(kMaxNq - c) << 12) | (uint32_t)q : 0xFFFFFFFFu;
   }
   __syncthreads();
   if (nq <= kRankSortMax) {
-    uint32_t* sorted = stage;  // free until the rows are packed
-    for (int q = tid; q < nq; q += kGroupThreads) {
+    for (int q = tid; q < nq; q += kOrderThreads) {
       const uint32_t kq = keys[q];
       int rank = 0;
 #pragma unroll 8
@@ -398,13 +351,12 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_
       sorted[rank] = kq;
     }
     __syncthreads();
-    for (int q = tid; q < nq; q += kGroupThreads) keys[q] = sorted[q];
-    __syncthreads();
-    n2 = 1;  // the bitonic passes below are skipped
+    for (int q = tid; q < nq; q += kOrderThreads) order[(size_t)h * nq + q] = (int32_t)(sorted[q] & 0xFFFu);
+    return;
   }
   for (int k = 2; k <= n2; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += kGroupThreads) {
+      for (int i = tid; i < n2; i += kOrderThreads) {
         const int l = i ^ j;
         if (l > i) {
           const uint32_t x = keys[i], y = keys[l];
@@ -416,196 +368,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_rows_kernel(const uint32_
       }
       __syncthreads();
     }
-  const int mc = min(max(*max_count, 0), nq);
-  const int cap = group_cost(mc, mc) * cap_num / cap_den;
-  int32_t* out = rows + (size_t)h * gh * kPlanRows;
-  // wavefront 0 packs the rows in order: the open group's union bitmask (words
-  // lane and lane + 64), the sum of its rows' counts (a bound on the union), its
-  // longest row m, its size, and its rows (lane s: row s).  The exact union size
-  // (a wavefront reduction) is only needed when the bound exceeds the cap.
-  uint32_t u0 = 0u, u1 = 0u;
-  int sum = 0, m = 0, gsize = 0, ng = 0, my_row = -1;
-  for (int c0 = 0; c0 < nq; c0 += kGroupChunk) {
-    const int nc = min(kGroupChunk, nq - c0);
-    __syncthreads();  // the previous chunk is consumed
-    for (int x = tid; x < nc * nwords; x += kGroupThreads) {
-      const int r = x / nwords, w = x - r * nwords;
-      const int q = (int)(keys[c0 + r] & 0xFFFu);
-      stage[x] = masks[((size_t)h * nq + q) * nwords + w];
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // row r's key and mask words, fetched one row ahead
-      uint32_t nkey = keys[c0];
-      uint32_t nw0 = lane < nwords ? stage[lane] : 0u;
-      uint32_t nw1 = lane + 64 < nwords ? stage[lane + 64] : 0u;
-      for (int r = 0; r < nc; ++r) {
-        const uint32_t key = __builtin_amdgcn_readfirstlane(nkey), w0 = nw0, w1 = nw1;
-        if (r + 1 < nc) {
-          nkey = keys[c0 + r + 1];
-          nw0 = lane < nwords ? stage[(r + 1) * nwords + lane] : 0u;
-          nw1 = lane + 64 < nwords ? stage[(r + 1) * nwords + lane + 64] : 0u;
-        }
-        const int q = (int)(key & 0xFFFu), cq = kMaxNq - (int)(key >> 12);
-        const int left = nq - (c0 + r);  // rows not yet placed, this one included
-        bool close = gsize == kPlanRows;
-        if (!close && gsize > 0 && group_cost(sum + cq, max(m, cq)) > cap &&
-            ng + 1 + (left + kPlanRows - 1) / kPlanRows <= gh) {
-          const int u = wave_sum_dpp(__popc(u0 | w0) + __popc(u1 | w1));
-          close = group_cost(u, max(m, cq)) > cap;
-        }
-        if (close) {
-          if (lane < kPlanRows) out[ng * kPlanRows + lane] = lane < gsize ? my_row : -1;
-          ++ng;
-          gsize = 0;
-          u0 = w0;
-          u1 = w1;
-          sum = cq;
-          m = cq;
-        } else {
-          u0 |= w0;
-          u1 |= w1;
-          sum += cq;
-          m = max(m, cq);
-        }
-        if (lane == gsize) my_row = q;
-        ++gsize;
-      }
-    }
-  }
-  if (tid < 64) {
-    if (gsize > 0) {
-      if (lane < kPlanRows) out[ng * kPlanRows + lane] = lane < gsize ? my_row : -1;
-      ++ng;
-    }
-    for (int x = ng * kPlanRows + lane; x < gh * kPlanRows; x += 64) out[x] = -1;
-  }
+  for (int q = tid; q < nq; q += kOrderThreads) order[(size_t)h * nq + q] = (int32_t)(keys[q] & 0xFFFu);
 }
 
-// one wavefront per group: load the rows' bitmask words at once, collect
-// (block, mask) tiles in ascending block order, bucket them by mask (a stable
-// counting sort, one ballot per mask value and chunk of 64 tiles), then fill
-// the trips greedily: lane m holds bucket m's remaining count, every lane scores
-// its mask, and a wave minimum picks one.  The group's entries go to its fixed
-// slot of nq entries and their number to counts[g], so a reader finds both
-// without a prefix sum (and can load them together); counts[groups] = nq.
-static_assert(kMasks <= 16, "one bucket per lane of the first 16-lane row");
-__global__ __launch_bounds__(64) void group_plan_kernel(const uint32_t* masks, int nq, int nwords, int gh,
-                                                        const int32_t* rows, int32_t* counts, int32_t* entries) {
-  __shared__ uint32_t wbuf[kPlanRows * (kMaxNq / 32)];
-  __shared__ int32_t tiles[kMaxNq];
-  __shared__ int32_t sorted_tiles[kMaxNq];
-  const int g = blockIdx.x, lane = threadIdx.x;
-  const int bh = g / gh;
-  if (g == 0 && lane == 0) counts[gridDim.x] = nq;
-  // the group's rows (valid ones first, -1 after)
-  int rq[kPlanRows], nr = 0, qlast = -1;
-#pragma unroll
-  for (int r = 0; r < kPlanRows; ++r) {
-    const int x = rows[(size_t)g * kPlanRows + r];
-    rq[r] = x >= 0 && x < nq ? x : -1;
-    if (rq[r] >= 0 && nr == r) ++nr;
-    qlast = max(qlast, rq[r]);
-  }
-  if (nr == 0) {
-    if (lane == 0) counts[g] = 0;
-    return;
-  }
-  const int words = (qlast >> 5) + 1;  // words covering key blocks 0 .. the last row
-  for (int x = lane; x < nr * words; x += 64) {
-    const int r = x / words, w = x - r * words;
-    int q = rq[0];
-#pragma unroll
-    for (int s = 1; s < kPlanRows; ++s)
-      if (r == s) q = rq[s];
-    wbuf[x] = masks[(size_t)(bh * nq + q) * nwords + w];
-  }
-  __syncthreads();
-  // ascending union tiles with their membership masks
-  int n = 0;
-  for (int w = 0; w < words; ++w) {
-    const int b = 32 * w + (lane & 31);
-    int m = 0;
-    if (lane < 32) {
-      for (int r = 0; r < nr; ++r) m |= (int)((wbuf[r * words + w] >> lane) & 1u) << r;
-    }
-    const uint64_t present = __ballot(m != 0);
-    if (m != 0) tiles[n + __popcll(present & ((1ull << lane) - 1ull))] = (b << 8) | m;
-    n += __popcll(present);
-  }
-  __syncthreads();
-  // bucket sizes (lane m: bucket m), then each tile's slot: its bucket's start
-  // plus the tiles of its bucket before it (stable)
-  int cnt = 0;
-  for (int t0 = 0; t0 < n; t0 += 64) {
-    const int m = t0 + lane < n ? tiles[t0 + lane] & (kMasks - 1) : -1;
-#pragma unroll
-    for (int v = 0; v < kMasks; ++v) {
-      const int c = __popcll(__ballot(m == v));
-      if (lane == v) cnt += c;
-    }
-  }
-  int start = cnt;  // exclusive prefix over the buckets
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(start, off);
-    if (lane >= off) start += y;
-  }
-  start -= cnt;
-  int fill = 0;  // lane m: tiles of bucket m placed so far
-  for (int t0 = 0; t0 < n; t0 += 64) {
-    const int t = t0 + lane;
-    const int e = t < n ? tiles[t] : 0;
-    const int m = t < n ? e & (kMasks - 1) : -1;
-    int dst = 0;
-#pragma unroll
-    for (int v = 0; v < kMasks; ++v) {
-      const uint64_t bal = __ballot(m == v);
-      const int base = __shfl(start + fill, v);
-      if (m == v) dst = base + __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == v) fill += __popcll(bal);
-    }
-    if (t < n) sorted_tiles[dst] = e;
-  }
-  __syncthreads();
-  int32_t* out = entries + (size_t)g * nq;  // the group's fixed slot of nq entries
-  if (lane == 0) counts[g] = n;
-  int left = lane < kMasks ? cnt : 0;  // lane m: tiles of bucket m not yet placed
-  int load[kPlanRows];
-  for (int k = 0; k < n;) {
-#pragma unroll
-    for (int w = 0; w < kPlanRows; ++w) load[w] = 0;
-    for (int slot = 0; slot < kPlanTrip && k < n; ++slot) {
-      // the mask whose tile raises the trip's busiest row the least; ties go to
-      // the mask covering more rows (more work per trip), then the lower mask
-      int key = 0x7fffffff;
-      if (lane >= 1 && lane < kMasks && left > 0) {
-        int mx = 0;
-#pragma unroll
-        for (int w = 0; w < kPlanRows; ++w) mx = max(mx, load[w] + ((lane >> w) & 1));
-        key = ((32 * mx - __popc(lane) + 32) << 8) | lane;
-      }
-      // minimum over lanes 0..15 (the masks), a prefix minimum by DPP row shifts
-      // that leaves it in lane 15
-      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x111, 0xF, 0xF, false));
-      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x112, 0xF, 0xF, false));
-      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x114, 0xF, 0xF, false));
-      key = min(key, __builtin_amdgcn_update_dpp(0x7fffffff, key, 0x118, 0xF, 0xF, false));
-      const int m = __builtin_amdgcn_readlane(key, 15) & (kMasks - 1);
-      // the bucket's last remaining tile (buckets drain from the top)
-      const int pos = __builtin_amdgcn_readlane(start + left - 1, m);
-      if (lane == m) --left;
-      if (lane == 0) out[k] = sorted_tiles[pos];
-#pragma unroll
-      for (int w = 0; w < kPlanRows; ++w) load[w] += (m >> w) & 1;
-      ++k;
-    }
-  }
-}
-
-size_t plan_capacity(int bh, int nq) {
-  const size_t groups = (size_t)bh * plan_groups_per_head(nq);
-  return groups + 1 + groups * kPlanRows + groups * (size_t)nq;
-}
+size_t plan_capacity(int bh, int nq) { return (size_t)bh * nq; }
 
 size_t support_workspace_bytes(int bh, int nq) {
   const size_t rows = (size_t)bh * nq;
@@ -651,10 +417,10 @@ hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t
   return hipGetLastError();
 }
 
-// CSR (row_ptr, col_idx, nnz) and, if plan != null, the execution plan from the
+// CSR (row_ptr, col_idx, nnz) and, if plan != null, the row order from the
 // per-row bitmasks and counts in the workspace
 static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz, int32_t* plan,
-                                  int plan_head_dim, void* workspace, hipStream_t stream) {
+                                  void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -668,29 +434,13 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, masks, nwords, row_ptr, col_idx);
   e = hipGetLastError();
   if (e != hipSuccess || plan == nullptr) return e;
-  // execution plan: plan[g] = entry count of group g, plan[groups] = the slot
-  // stride nq, group g's rows at plan + groups + 1 + kPlanRows * g, its entries
-  // at plan + groups + 1 + kPlanRows * groups + g * nq
-  const int gh = plan_groups_per_head(nq);
-  const int groups = bh * gh;
-  int32_t* plan_rows = plan + groups + 1;
-  // group cap relative to the longest row's cost: 9/10 for the head_dim 64
-  // kernel (three workgroups per CU, more slots than groups, so the longest
-  // groups decide its end), 5/4 for the others
-  const int cap_num = plan_head_dim == 64 ? 9 : 3, cap_den = plan_head_dim == 64 ? 10 : 2;
-  hipLaunchKernelGGL(group_rows_kernel, dim3(bh), dim3(kGroupThreads), 0, stream, masks, counts, max_count, nq,
-                     nwords, gh, cap_num, cap_den, plan_rows);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(group_plan_kernel, dim3(groups), dim3(64), 0, stream, masks, nq, nwords, gh, plan_rows, plan,
-                     plan_rows + (size_t)kPlanRows * groups);
+  hipLaunchKernelGGL(order_rows_kernel, dim3(bh), dim3(kOrderThreads), 0, stream, counts, nq, plan);
   return hipGetLastError();
 }
 
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
                           const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, int32_t* plan, int plan_head_dim, void* workspace,
-                          hipStream_t stream) {
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -710,7 +460,7 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, plan_head_dim, workspace, stream);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
 }
 
 // ---------------------------------------------------------------- coarser blocks
@@ -770,7 +520,7 @@ size_t support_blocked_workspace_bytes(int bh, int nq, int steps, int f) {
 }
 
 hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, double eta, int f, int32_t* row_ptr,
-                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, int plan_head_dim, void* workspace,
+                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace,
                                   hipStream_t stream) {
   const int nqb = nq / f;
   const int nwb = (nqb + 31) / 32;
@@ -808,7 +558,7 @@ hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, 
                      masks, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, plan_head_dim, workspace, stream);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
 }
 
 }  // namespace wise

@@ -43,17 +43,16 @@ float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.
 wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
                      const void* q, const void* k, const void* v, void* o, float* lse, float* mass,
                      float* mass_ws, const int32_t* row_ptr, const int32_t* col_idx, int64_t col_cap, const int32_t* plan,
-                     int64_t plan_cap, bool sparse, float scale, void* stream) {
+                     bool sparse, float scale, void* stream) {
   const bool b16 = block == kBlock / 2;
   if (col_cap > INT32_MAX) col_cap = INT32_MAX;
-  if (plan_cap > INT32_MAX) plan_cap = INT32_MAX;
   const int nq = seqlen / kBlock;
   const int rows = batch * heads * nq;
   const float sc = resolve_scale(scale, head_dim);
   hipError_t e;
   if (dt == WISE_BF16) {
     AttnBf16Args a{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                   static_cast<__bf16*>(o), lse, mass, mass_ws, row_ptr, col_idx, col_cap, plan, plan_cap, seqlen, nq, rows,
+                   static_cast<__bf16*>(o), lse, mass, mass_ws, row_ptr, col_idx, col_cap, plan, seqlen, nq, rows,
                    heads, heads / kv_heads, sc * 1.4426950408889634f};
     e = launch_attn_bf16(a, head_dim, sparse, mass != nullptr, b16, static_cast<hipStream_t>(stream));
   } else {
@@ -69,7 +68,7 @@ wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seql
 // workspace_need: bytes of workspace the builder needs (0: the plain builder's)
 wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_t* row_ptr, int32_t* col_idx,
                         int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
-                        int plan_head_dim, void* workspace, size_t workspace_bytes, size_t workspace_need = 0) {
+                        void* workspace, size_t workspace_bytes, size_t workspace_need = 0) {
   if (bh <= 0 || nq <= 0 || nq > 4096 || num_steps <= 0 || num_steps > 64) return WISE_ERR_INVALID_ARG;
   if (!mass || !row_ptr || !col_idx || !nnz || !workspace) return WISE_ERR_INVALID_ARG;
   if (!aligned4(mass) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(nnz) || !aligned16(workspace))
@@ -81,8 +80,6 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
   if (plan != nullptr) {
     const size_t need = wise_build_support_plan_capacity(bh, nq);
     if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
-    if (plan_head_dim != 0 && plan_head_dim != 64 && plan_head_dim != 96 && plan_head_dim != 128)
-      return WISE_ERR_INVALID_ARG;
   }
   return WISE_OK;
 }
@@ -153,7 +150,7 @@ wise_status wise_full_attn_mass(wise_dtype dt, int batch, int heads, int kv_head
     ws = static_cast<float*>(workspace);
   }
   return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, mass, ws, nullptr, nullptr,
-                  0, nullptr, 0, false, scale, stream);
+                  0, nullptr, false, scale, stream);
 }
 
 wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
@@ -177,20 +174,19 @@ size_t wise_build_support_plan_capacity(int bh, int nq) {
 
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta, int32_t* row_ptr,
                                int32_t* col_idx, int64_t col_capacity, int32_t* nnz, int32_t* plan,
-                               int64_t plan_capacity, int plan_head_dim, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int64_t plan_capacity, void* workspace, size_t workspace_bytes, void* stream) {
   wise_status st = check_build(bh, nq, num_steps, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
-                               plan_head_dim, workspace, workspace_bytes);
+                               workspace, workspace_bytes);
   if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, 0, nullptr, nullptr, 0, row_ptr, col_idx, nnz,
-                                plan, plan_head_dim, workspace, static_cast<hipStream_t>(stream));
+                                plan, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
 wise_status wise_build_support_static(int bh, int nq, int num_steps, const float* mass, float eta,
                                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
-                                      int32_t* plan, int64_t plan_capacity, int plan_head_dim, void* stream) {
+                                      int32_t* plan, int64_t plan_capacity, void* stream) {
   const size_t need = wise_build_support_workspace_bytes(bh, nq, num_steps);
   if (need == 0) return WISE_ERR_INVALID_ARG;
   if (need > WISE_STATIC_SCRATCH_BYTES) return WISE_ERR_UNSUPPORTED;
@@ -198,7 +194,7 @@ wise_status wise_build_support_static(int bh, int nq, int num_steps, const float
   const wise_status st = static_scratch(&ws);
   if (st != WISE_OK) return st;
   return wise_build_support(bh, nq, num_steps, mass, eta, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
-                            plan_head_dim, ws, need, stream);
+                            ws, need, stream);
 }
 
 size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps, int block) {
@@ -212,22 +208,22 @@ size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps,
 
 wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps, const float* mass, float eta,
                                        int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* nnz,
-                                       int32_t* plan, int64_t plan_capacity, int plan_head_dim, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+                                       int32_t* plan, int64_t plan_capacity, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   if (block == kBlock)
     return wise_build_support(bh, nq, num_steps, mass, eta, row_ptr, col_idx, col_capacity, nnz, plan,
-                              plan_capacity, plan_head_dim, workspace, workspace_bytes, stream);
+                              plan_capacity, workspace, workspace_bytes, stream);
   if (block != 2 * kBlock && block != 4 * kBlock) return WISE_ERR_UNSUPPORTED;
   const int f = block / kBlock;
   if (nq <= 0 || nq % f != 0) return WISE_ERR_INVALID_ARG;
   const size_t need = wise_build_support_blocked_workspace_bytes(bh, nq, num_steps, block);
   if (need == 0) return WISE_ERR_INVALID_ARG;
   wise_status st = check_build(bh, nq, num_steps, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
-                               plan_head_dim, workspace, workspace_bytes, need);
+                               workspace, workspace_bytes, need);
   if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support_blocked(mass, bh, nq, num_steps, (double)eta, f, row_ptr, col_idx, nnz, plan,
-                                        plan_head_dim, workspace, static_cast<hipStream_t>(stream));
+                                        workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -235,9 +231,9 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
                                        const int32_t* ref_row_ptr, const int32_t* ref_col_idx,
                                        int64_t ref_col_capacity, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
-                                       int plan_head_dim, void* workspace, size_t workspace_bytes, void* stream) {
+                                       void* workspace, size_t workspace_bytes, void* stream) {
   wise_status st = check_build(bh, nq, 1, mass, row_ptr, col_idx, col_capacity, nnz, plan, plan_capacity,
-                               plan_head_dim, workspace, workspace_bytes);
+                               workspace, workspace_bytes);
   if (st != WISE_OK) return st;
   int k;
   switch (kind) {
@@ -259,7 +255,7 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
     if (!aligned4(ref_row_ptr) || !aligned4(ref_col_idx)) return WISE_ERR_INVALID_ARG;
   }
   hipError_t e = launch_support(mass, bh, nq, 1, (double)eta, k, ref_row_ptr, ref_col_idx, ref_col_capacity, row_ptr,
-                                col_idx, nnz, plan, plan_head_dim, workspace, static_cast<hipStream_t>(stream));
+                                col_idx, nnz, plan, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -285,7 +281,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
   // 16-token rows are bitmasks of 2048 blocks in both kernels' LDS
   if (block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
   if (plan != nullptr) {
-    // every group's fixed slot must be readable
+    // the row order holds one entry per row
     const int64_t bh = (int64_t)batch * heads;
     const size_t need = bh <= INT32_MAX ? wise_build_support_plan_capacity((int)bh, seqlen / kBlock) : 0;
     if (!aligned4(plan) || need == 0 || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
@@ -293,7 +289,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
     if (dt != WISE_BF16 || block != kBlock) plan = nullptr;
   }
   return run_attn(dt, batch, heads, kv_heads, seqlen, head_dim, block, q, k, v, o, lse, nullptr, nullptr, row_ptr, col_idx,
-                  col_capacity, plan, plan_capacity, true, scale, stream);
+                  col_capacity, plan, true, scale, stream);
 }
 
 }  // extern "C"

@@ -19,7 +19,7 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes",
     "wise_dense_attn",
@@ -51,20 +51,19 @@ def _load():
     lib.wise_build_support.restype = i32
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
-    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp, ctypes.c_size_t,
-                                       vp]
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
     lib.wise_build_support_blocked_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_blocked_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.wise_build_support_blocked.restype = i32
-    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp,
+    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp,
                                                ctypes.c_size_t, vp]
     lib.wise_build_support_variant.restype = i32
-    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, i32,
+    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64,
                                                vp, ctypes.c_size_t, vp]
     lib.wise_retained_mass.restype = i32
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_build_support_static.restype = i32
-    lib.wise_build_support_static.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp]
+    lib.wise_build_support_static.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp]
     lib.wise_sparse_attn.restype = i32
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
                                      f32, vp]
@@ -212,7 +211,8 @@ def build_support_plan_capacity(bh: int, nq: int) -> int:
 
 class Schedule:
     """Device-resident CSR schedule: row_ptr [rows+1], col_idx [capacity], nnz [1] (int32),
-    and optionally the execution plan of the same schedule (int32, or None)."""
+    and optionally its row order (int32 [rows]: each head's query blocks, longest
+    scheduled row first), or None."""
 
     def __init__(self, row_ptr, col_idx, nnz, bh, nq, plan=None):
         self.row_ptr, self.col_idx, self.nnz, self.bh, self.nq = row_ptr, col_idx, nnz, bh, nq
@@ -239,11 +239,10 @@ def _plan_args(schedule: Schedule):
 
 
 def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspace=None, stream=None,
-                  with_plan: bool = True, block: int = BLOCK, plan_head_dim: int = 0):
-    """Selection + temporal union + CSR (+ execution plan) from 32-token masses
+                  with_plan: bool = True, block: int = BLOCK):
+    """Selection + temporal union + CSR (+ row order) from 32-token masses
     [num_steps, b*h, nq, nq] (fp32).  block = 64 or 128 selects at that block size
-    (the schedule stays at 32-token granularity); plan_head_dim is the head
-    dimension of the sparse attention that will use the plan (0: not known)."""
+    (the schedule stays at 32-token granularity)."""
     if mass.dim() != 4 or mass.shape[2] != mass.shape[3]:
         raise ValueError("mass must be [num_steps, batch*heads, nq, nq]")
     if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda:
@@ -258,14 +257,13 @@ def build_support(mass, eta: float, *, schedule: Schedule | None = None, workspa
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=mass.device)
     st = lib.wise_build_support_blocked(block, bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
                                         _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
-                                        *_plan_args(schedule), int(plan_head_dim), _ptr(workspace), workspace.numel(),
-                                        _stream(stream))
+                                        *_plan_args(schedule), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "wise_build_support_blocked" if block != BLOCK else "wise_build_support")
     return schedule
 
 
 def build_support_static(mass, eta: float, *, schedule: Schedule | None = None, stream=None,
-                         with_plan: bool = True, plan_head_dim: int = 0):
+                         with_plan: bool = True):
     """build_support at block 32 through wise_build_support_static, which takes
     no workspace and allocates nothing (its scratch is the library's own device
     array); the schedule buffers are the caller's, as always."""
@@ -278,7 +276,7 @@ def build_support_static(mass, eta: float, *, schedule: Schedule | None = None, 
         schedule = alloc_schedule(bh, nq, mass.device, with_plan=with_plan)
     st = lib.wise_build_support_static(bh, nq, steps, _ptr(mass), float(eta), _ptr(schedule.row_ptr),
                                        _ptr(schedule.col_idx), schedule.col_idx.numel(), _ptr(schedule.nnz),
-                                       *_plan_args(schedule), int(plan_head_dim), _stream(stream))
+                                       *_plan_args(schedule), _stream(stream))
     _check(st, "wise_build_support_static")
     return schedule
 
@@ -288,8 +286,7 @@ _VARIANTS = {"static": SUPPORT_STATIC, "size_matched": SUPPORT_SIZE_MATCHED, "ma
 
 
 def build_support_variant(kind, mass, *, eta: float = 0.95, reference: Schedule | None = None,
-                          schedule: Schedule | None = None, workspace=None, stream=None, with_plan: bool = True,
-                          plan_head_dim: int = 0):
+                          schedule: Schedule | None = None, workspace=None, stream=None, with_plan: bool = True):
     """Intervention-control schedule from one step's masses [b*h, nq, nq] (fp32):
     kind "static" (cumulative-eta support), "size_matched" or "mass_matched" (against
     the reference schedule)."""
@@ -313,8 +310,8 @@ def build_support_variant(kind, mass, *, eta: float = 0.95, reference: Schedule 
     ref_cap = reference.col_idx.numel() if reference is not None else 0
     st = lib.wise_build_support_variant(code, bh, nq, _ptr(mass), float(eta), ref_rp, ref_ci, ref_cap,
                                         _ptr(schedule.row_ptr), _ptr(schedule.col_idx), schedule.col_idx.numel(),
-                                        _ptr(schedule.nnz), *_plan_args(schedule), int(plan_head_dim),
-                                        _ptr(workspace), workspace.numel(), _stream(stream))
+                                        _ptr(schedule.nnz), *_plan_args(schedule), _ptr(workspace), workspace.numel(),
+                                        _stream(stream))
     _check(st, "wise_build_support_variant")
     return schedule
 
@@ -336,9 +333,9 @@ def retained_mass(mass, schedule: Schedule, *, out=None, stream=None):
 
 def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=False, scale=None,
                 block=BLOCK, stream=None):
-    """Block-sparse causal attention over a CSR schedule (walking its execution plan when it
-    carries one).  block 16 takes a 16-token schedule (build_support on 16-token masses;
-    no plan).  Returns (out, lse)."""
+    """Block-sparse causal attention over a CSR schedule (starting rows in its row order
+    when it carries one).  block 16 takes a 16-token schedule (build_support on 16-token
+    masses; no row order).  Returns (out, lse)."""
     b, h, hk, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     if want_lse and lse is None:

@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 9
+#define WISE_ABI_VERSION 10
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -116,11 +116,8 @@ wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, i
 size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
 
 /*
- * int32 entries of the optional execution plan wise_build_support can emit
- * beside the CSR schedule for bh rows of nq query blocks (0 on invalid sizes):
- * G + 1 + 4*G + G*nq with G = bh * (ceil(nq / 4) + ceil(nq / 16)) query-block
- * groups (G entry counts, the slot stride, 4 row indices per group, and a fixed
- * slot of nq entries per group).
+ * int32 entries of the optional row order wise_build_support can emit beside
+ * the CSR schedule for bh rows of nq query blocks: bh * nq (0 on invalid sizes).
  */
 size_t wise_build_support_plan_capacity(int bh, int nq);
 
@@ -143,38 +140,14 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *   col_idx     : int32 [col_capacity], written; ascending within a row.
  *   col_capacity: must be >= bh*nq*(nq+1)/2 (the fully dense worst case).
  *   nnz         : int32 device scalar, written with row_ptr[bh*nq].
- *   plan        : NULL, or int32 [plan_capacity] receiving the execution plan of
- *                 the same schedule (the execution metadata the WISE paper, App. B,
+ *   plan        : NULL, or int32 [plan_capacity] receiving the row order of the
+ *                 same schedule (the execution metadata the WISE paper, App. B,
  *                 prepares with the sparse schedule), with
- *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq).
- *                 The query blocks of each (batch, head) are dealt to
- *                 GH = ceil(nq/4) + ceil(nq/16) groups of at most 4 blocks;
- *                 group g = bh_index*GH + j, j = 0 .. GH-1.  A head's blocks are
- *                 taken in order of scheduled block count, longest first (ties:
- *                 lower index first), and packed 4 to a group, except that a
- *                 group is closed early when its next block would raise its
- *                 estimated run time (9 per started run of 4 union blocks plus 4
- *                 per block of its longest row) above a cap, as long as the
- *                 blocks left fit in
- *                 the groups left; groups are numbered in the order they are
- *                 closed, and those left over list no blocks.  plan[g] (g < G) is
- *                 group g's entry count n_g, plan[G] = nq the slot stride,
- *                 plan[G + 1 + 4*g + w] (w < 4) the group's query block w or -1
- *                 (its blocks first), and group g's entries are
- *                 plan[5*G + 1 + g*nq .. 5*G + g*nq + n_g] (a fixed slot, so a
- *                 reader loads the count and the first entries at once); each
- *                 entry is (key block << 8) | membership, bit w of the
- *                 membership set iff the group's query block w lists that key
- *                 block.  Each key block of the group's union appears once, in
- *                 runs of 2 (the tiles the kernel holds at once) that spread
- *                 the member rows' blocks evenly.
- *   plan_head_dim: the head dimension of the bf16 sparse attention that will
- *                 walk the plan (64, 96 or 128), or 0 if not known; it sets the
- *                 group cap: 9/10 of the longest row's cost at 64 (three
- *                 workgroups per CU there, so the longest groups decide the
- *                 kernel's end), 3/2 otherwise.  Any value gives a valid plan
- *                 for every head dimension; others than these four are
- *                 rejected when plan is not NULL, ignored when it is.
+ *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq):
+ *                 plan[bh_index*nq + j], j = 0 .. nq-1, lists the query blocks
+ *                 of (batch, head) bh_index in order of scheduled block count,
+ *                 longest first (ties: lower index first) -- a permutation of
+ *                 0 .. nq-1, the order the bf16 sparse kernel starts its rows in.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.
@@ -182,7 +155,7 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  */
 wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass, float eta,
                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                               int32_t* nnz, int32_t* plan, int64_t plan_capacity, int plan_head_dim,
+                               int32_t* nnz, int32_t* plan, int64_t plan_capacity,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -202,8 +175,7 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
 #define WISE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
 wise_status wise_build_support_static(int bh, int nq, int num_steps, const float* mass, float eta,
                                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                                      int32_t* nnz, int32_t* plan, int64_t plan_capacity, int plan_head_dim,
-                                      void* stream);
+                                      int32_t* nnz, int32_t* plan, int64_t plan_capacity, void* stream);
 
 /*
  * Working-set schedule selected at a coarser block size (the block-size study of
@@ -212,7 +184,7 @@ wise_status wise_build_support_static(int bh, int nq, int num_steps, const float
  * writes; the block-level mass of Eq. 5 at block B is (32/B) times the sum of
  * the (B/32)^2 32-token masses it covers (Eq. 5 is linear in A), accumulated in
  * fp64 and rounded to fp32.  The cumulative-eta support and the union over the
- * steps are taken at block B; the output schedule (and plan) stays at the
+ * steps are taken at block B; the output schedule (and row order) stays at the
  * 32-token granularity the sparse kernel runs on: 32-token query block q lists
  * every 32-token key block k <= q whose B-block is selected for q's B-block --
  * exactly the keys the B-level reuse mask admits.
@@ -225,7 +197,7 @@ size_t wise_build_support_blocked_workspace_bytes(int bh, int nq, int num_steps,
 wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps, const float* mass,
                                        float eta, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int32_t* nnz, int32_t* plan,
-                                       int64_t plan_capacity, int plan_head_dim, void* workspace,
+                                       int64_t plan_capacity, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
 /*
@@ -248,7 +220,8 @@ wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps,
  *                   WISE working set), matched kinds only (may be NULL for
  *                   STATIC); entries outside 0..q are ignored, duplicates count
  *                   once.
- *   the outputs, plan and workspace are as for wise_build_support (num_steps 1).
+ *   the outputs, row order and workspace are as for wise_build_support
+ *   (num_steps 1).
  */
 typedef enum {
   WISE_SUPPORT_STATIC = 0,
@@ -260,7 +233,7 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
                                        const int32_t* ref_row_ptr, const int32_t* ref_col_idx,
                                        int64_t ref_col_capacity, int32_t* row_ptr, int32_t* col_idx,
                                        int64_t col_capacity, int32_t* nnz, int32_t* plan, int64_t plan_capacity,
-                                       int plan_head_dim, void* workspace, size_t workspace_bytes, void* stream);
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Retained attention mass of a schedule (the WISE paper, App. B: the fraction of
@@ -292,21 +265,25 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  *                            kernels mask the unscheduled 16 x 16 sub-blocks of the
  *                            32 x 32 tiles they visit.
  *   col_capacity           : number of readable col_idx entries.
- *   plan, plan_capacity    : NULL, or the execution plan wise_build_support wrote
- *                            for this same schedule, plan_capacity its readable
- *                            int32 entries (at least
+ *   plan, plan_capacity    : NULL, or the row order wise_build_support wrote for
+ *                            this same schedule, plan_capacity its readable int32
+ *                            entries (at least
  *                            wise_build_support_plan_capacity(batch*heads,
- *                            seqlen / 32), else WISE_ERR_INVALID_ARG).  When given, the bf16
- *                            kernel walks the plan instead of the CSR rows (same
- *                            result up to the order of floating-point summation);
- *                            the fp32 kernel and block 16 ignore it.
- * Entries outside 0..q, CSR offsets outside 0..col_capacity and plan entry
- * counts outside 0..nq are ignored (clamped).  In the CSR a block listed twice counts once; a plan must come
- * from wise_build_support, which lists each block of a group once.  A row left
- * with no admissible key writes o = 0 and lse = -inf (wise_build_support never
- * produces one).  Both kernels support up to 4096 key blocks per head
- * (seqlen <= 131072), and up to 2048 at block 16 (seqlen <= 32768); beyond
- * that WISE_ERR_UNSUPPORTED is returned.
+ *                            seqlen / 32), else WISE_ERR_INVALID_ARG).  The bf16
+ *                            kernel at block 32 gives every query block one
+ *                            wavefront of its own, which walks the block's CSR
+ *                            row; with a row order it starts each head's rows
+ *                            in that order (longest first), without one in
+ *                            descending query-block order.  The results do not
+ *                            depend on it; the fp32 kernel and block 16 ignore it.
+ * Entries outside 0..q and CSR offsets outside 0..col_capacity are ignored
+ * (clamped); a block listed twice counts once.  A row order must be a
+ * permutation of each head's query blocks, as wise_build_support writes it
+ * (entries outside 0..nq-1 are skipped, and a row it does not list is not
+ * computed).  A row left with no admissible key writes o = 0 and lse = -inf
+ * (wise_build_support never produces one).  Both kernels support up to 4096 key
+ * blocks per head (seqlen <= 131072), and up to 2048 at block 16
+ * (seqlen <= 32768); beyond that WISE_ERR_UNSUPPORTED is returned.
  */
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
                              int head_dim, int block, const void* q, const void* k, const void* v, void* o,

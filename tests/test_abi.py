@@ -40,14 +40,13 @@ def lib():
     lib.wise_build_support_workspace_bytes.argtypes = [i32, i32, i32]
     lib.wise_build_support_plan_capacity.restype = ctypes.c_size_t
     lib.wise_build_support_plan_capacity.argtypes = [i32, i32]
-    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp, ctypes.c_size_t,
-                                       vp]
-    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64, i32,
+    lib.wise_build_support.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, ctypes.c_size_t, vp]
+    lib.wise_build_support_variant.argtypes = [i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64,
                                                vp, ctypes.c_size_t, vp]
     lib.wise_retained_mass.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp]
     lib.wise_build_support_blocked_workspace_bytes.restype = ctypes.c_size_t
     lib.wise_build_support_blocked_workspace_bytes.argtypes = [i32, i32, i32, i32]
-    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, i32, vp,
+    lib.wise_build_support_blocked.argtypes = [i32, i32, i32, i32, vp, f32, vp, vp, i64, vp, vp, i64, vp,
                                                ctypes.c_size_t, vp]
     lib.wise_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64,
                                      f32, vp]
@@ -70,7 +69,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 9
+    assert lib.wise_abi_version() == 10
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -142,18 +141,16 @@ def test_workspace_bytes(lib):
 def test_plan_capacity(lib):
     f = lib.wise_build_support_plan_capacity
     assert f(0, 8) == 0 and f(1, 0) == 0 and f(1, 4097) == 0
-    # group entry counts and the slot stride (G + 1), four row indices per group,
-    # and a fixed slot of nq entries per group
+    # one row-order entry per (head, query block)
     for bh, nq in ((1, 8), (32, 128), (3, 33), (1, 1)):
-        g = bh * ((nq + 3) // 4 + (nq + 15) // 16)
-        assert f(bh, nq) == g + 1 + 4 * g + g * nq
+        assert f(bh, nq) == bh * nq
 
 
-def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0, hd=0,
+def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0,
            ws=P2, wsb=None):
     cap = bh * nq * (nq + 1) // 2 if cap is None else cap
     wsb = lib.wise_build_support_workspace_bytes(bh, nq, steps) if wsb is None else wsb
-    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, plan, pcap, hd, ws, wsb, None)
+    return lib.wise_build_support(bh, nq, steps, mass, eta, rp, ci, cap, nnz, plan, pcap, ws, wsb, None)
 
 
 def test_build_support_validation(lib):
@@ -170,8 +167,6 @@ def test_build_support_validation(lib):
     need = lib.wise_build_support_plan_capacity(2, 8)
     assert _build(lib, plan=P, pcap=need - 1) == INVALID
     assert _build(lib, plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
-    for hd in (-1, 1, 32, 80, 256):                      # plan head dimension: 0, 64, 96 or 128
-        assert _build(lib, plan=P, pcap=need, hd=hd) == INVALID, hd
     # a worst case beyond int32 row offsets is rejected
     assert _build(lib, bh=1 << 20, nq=4096, cap=1 << 62, wsb=1 << 62) == INVALID
 
@@ -197,9 +192,9 @@ def test_sparse_validation(lib):
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
     assert sp(d=80) == UNSUPPORTED
-    need = lib.wise_build_support_plan_capacity(1, 4)    # 2 groups: counts, stride, rows, 4 entry slots each
-    assert need == 2 + 1 + 2 * 4 + 2 * 4
-    assert sp(plan=P, pcap=need - 1) == INVALID         # a group slot would be out of reach
+    need = lib.wise_build_support_plan_capacity(1, 4)    # one row-order entry per query block
+    assert need == 4
+    assert sp(plan=P, pcap=need - 1) == INVALID         # a row would be out of reach
     assert sp(plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
 
 
@@ -209,7 +204,7 @@ def test_variant_and_retained_validation(lib):
     wsb = lib.wise_build_support_workspace_bytes(bh, nq, 1)
 
     def var(kind=1, mass=P, eta=0.95, rrp=P, rci=P, rcap=10, rp=P, ci=P, c=cap, nnz=P, ws=P2, w=wsb):
-        return lib.wise_build_support_variant(kind, bh, nq, mass, eta, rrp, rci, rcap, rp, ci, c, nnz, NULL, 0, 0,
+        return lib.wise_build_support_variant(kind, bh, nq, mass, eta, rrp, rci, rcap, rp, ci, c, nnz, NULL, 0,
                                               ws, w, None)
     assert var(kind=3) == INVALID and var(kind=-1) == INVALID
     assert var(kind=0, eta=0.0) == INVALID and var(kind=0, eta=1.5) == INVALID
@@ -244,7 +239,7 @@ def test_blocked_builder_validation(lib):
     def blk(block=64, bh=2, nq=8, steps=4, eta=0.95, cap=None, ws=P2, wsb=None):
         cap = bh * nq * (nq + 1) // 2 if cap is None else cap
         wsb = (f(bh, nq, steps, block) or 1 << 20) if wsb is None else wsb
-        return lib.wise_build_support_blocked(block, bh, nq, steps, P, eta, P, P, cap, P, NULL, 0, 0, ws, wsb, None)
+        return lib.wise_build_support_blocked(block, bh, nq, steps, P, eta, P, P, cap, P, NULL, 0, ws, wsb, None)
     assert blk(block=48) == UNSUPPORTED and blk(block=16) == UNSUPPORTED
     assert blk(nq=9) == INVALID                 # not a whole number of 64-token blocks
     assert blk(wsb=f(2, 8, 4, 64) - 1) == INVALID
@@ -257,11 +252,10 @@ def test_static_builder_rejects_shapes_beyond_its_scratch(lib):
     f = lib.wise_build_support_static
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                  ctypes.c_void_p]
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     need = lib.wise_build_support_workspace_bytes(241, 512, 4)
     assert need > 8 << 20 >= lib.wise_build_support_workspace_bytes(240, 512, 4)
-    args = (P2, 0.95, P2, P2, 1 << 40, P2, None, 0, 128, None)
+    args = (P2, 0.95, P2, P2, 1 << 40, P2, None, 0, None)
     assert f(241, 512, 4, *args) == UNSUPPORTED
     assert f(1, 8192, 4, *args) == INVALID        # nq beyond 4096
     assert f(0, 128, 4, *args) == INVALID
