@@ -944,29 +944,34 @@ __global__ __launch_bounds__(64 * kSparseWaves) __attribute__((
 //
 // Block-sparse attention at 32-token blocks.  A reuse-step row's scheduled key
 // blocks are mostly its own (the selected blocks of neighbouring query blocks
-// overlap little: at 4k, four-row groups would use 39% of their wavefront
-// steps), so a workgroup is one wavefront owning one query block.  It streams
-// its row's blocks through one LDS slot of its own, with no barrier and no
-// idle wavefront: at the start of a step the block's K and V operands move from
-// the slot to registers, the slot refills with the next block, and the block
-// is computed from the registers while that copy runs.  Two such wavefronts
-// share each SIMD, so one's copy waits, row set-up and output stores overlap
-// the other's matrix work.
+// overlap little: at 4k, four-row groups walking the union of their rows would
+// use 39% of their wavefront steps), so each work unit -- a query block's row,
+// or a part of a long row -- gets one wavefront that streams the unit's blocks
+// through one LDS slot of its own, with no barrier: at the start of a step the
+// block's K and V operands move from the slot to registers, the slot refills
+// with the next block, and the block is computed from the registers while that
+// copy runs.  Two wavefronts share each SIMD, so one's copy waits, set-up and
+// output stores overlap the other's matrix work.  A workgroup runs a bundle of
+// kUnitBundle units; a split row's parts share a bundle and merge through LDS
+// after the bundle's one barrier: with L_p the parts' log-sum-exps (log2 units)
+// and O_p their normalised outputs, L = log2 sum_p 2^L_p and
+// O = sum_p 2^(L_p - L) O_p.
 //
-// The row's blocks are walked in ascending order from a bitmask over key blocks
-// held in two VGPRs (word w in lane w % 64 of register w / 64), built from the
-// CSR row: entries outside 0..qb are ignored and duplicates count once.
+// A unit's blocks are walked in ascending order from a bitmask over key blocks
+// held in two VGPRs (word w in lane w % 64 of register w / 64), built from its
+// CSR entries: entries outside 0..qb are ignored and duplicates count once.
 
-// LDS bytes of one row-stream workgroup: one slot of a K and a V tile.
+// LDS bytes of one row-stream wavefront: one slot of a K and a V tile.
 template <int D>
 constexpr int rows_lds_bytes() {
   return 2 * Tile<D>::BYTES;
 }
-// Row-stream workgroups resident per CU: two wavefronts per SIMD, within the
+// Row-stream wavefronts resident per CU: two per SIMD, whole bundles within the
 // 160 KiB of LDS.
 template <int D>
 constexpr int rows_per_cu() {
-  return (160 * 1024) / rows_lds_bytes<D>() < 8 ? (160 * 1024) / rows_lds_bytes<D>() : 8;
+  constexpr int by_lds = (160 * 1024) / (kUnitBundle * rows_lds_bytes<D>()) * kUnitBundle;
+  return by_lds < kRowWavesPerCu ? by_lds : kRowWavesPerCu;
 }
 
 // Ascending walk over the set bits of a row bitmask of nw words.
@@ -998,23 +1003,27 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_rows_kernel(AttnBf16Args a) {
+__global__ __launch_bounds__(64 * kUnitBundle) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_rows_kernel(
+    AttnBf16Args a) {
   using T = Tile<D>;
   constexpr int CI = D / 16;  // wave-copies per tile
-  __shared__ __attribute__((aligned(1024))) unsigned char slot[2 * T::BYTES];  // K tile, then V tile
-  static_assert(sizeof(slot) == rows_lds_bytes<D>(), "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char slots[kUnitBundle][2 * T::BYTES];  // K tile, then V tile
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 31, h = lane >> 5;
+  unsigned char* const slot = slots[wave];
   const int bhn = a.rows / a.nq;
-  // rank r of a head: its r-th row in the schedule's row order (longest first),
-  // or query block nq - 1 - r without one (later rows tend to be longer)
-  const int per_head = a.nq;
+  // bundle r of a head: its unit slots kUnitBundle r .. kUnitBundle r + 3 (the
+  // units longest first within their split class), or without units query
+  // blocks nq - 1 - kUnitBundle r - w (later rows tend to be longer)
+  const int cap = a.plan != nullptr ? unit_slots(a.nq) : a.nq;
+  const int per_head = (cap + kUnitBundle - 1) / kUnitBundle;
   // XCD-aligned head runs taken hg heads at a time, as in the streaming kernel,
-  // hg the fewest heads whose rows fill the XCD's workgroup slots twice over: a
-  // row is one wavefront's serial work, so the longest rows of all the heads in
-  // flight have to start in the first rounds of slots; a larger hg would only
-  // spread the XCD's L2 over more heads' K and V
+  // hg the fewest heads whose rows fill the XCD's wavefront slots twice over: a
+  // unit is one wavefront's serial work, so the longest units of all the heads
+  // in flight have to start in the first rounds of slots; a larger hg would
+  // only spread the XCD's L2 over more heads' K and V
   int bh, rank;
   {
     constexpr int kSlotsPerXcd = 32 * rows_per_cu<D>();
@@ -1022,19 +1031,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int base = bhn >> 3, rem = bhn & 7;
     const int run = base + (x < rem ? 1 : 0), start = x * base + min(x, rem);
     if (k >= run * per_head) return;
-    const int hg = min(run, max(1, (2 * kSlotsPerXcd + per_head - 1) / per_head));
+    const int hg = min(run, max(1, (2 * kSlotsPerXcd + a.nq - 1) / a.nq));
     const int c = k / (hg * per_head), within = k - c * hg * per_head;
     const int hc = min(hg, run - c * hg);
     bh = start + c * hg + within % hc;
     rank = within / hc;
   }
-  int qb;
+  // this wavefront's unit: query block qb, part `part` of `parts` (qb < 0: none)
+  const int s = kUnitBundle * rank + wave;
+  int qb = -1, part = 0, parts = 1;
   if (a.plan != nullptr) {
-    qb = a.plan[(size_t)bh * a.nq + rank];
-    if (qb < 0 || qb >= a.nq) return;  // not a row (a row order from the builder has none)
-  } else {
-    qb = a.nq - 1 - rank;
+    const int units = min(a.plan[bh], cap);
+    if (kUnitBundle * rank >= units) return;  // an empty bundle (uniform over the workgroup)
+    const int u = s < units ? a.plan[bhn + (size_t)bh * cap + s] : -1;
+    if (u >= 0 && (u >> 8) < a.nq && ((u >> 4) & 15) < (u & 15) + 1 && (u & 15) < kUnitBundle &&
+        wave - ((u >> 4) & 15) >= 0 && wave - ((u >> 4) & 15) + (u & 15) < kUnitBundle) {
+      qb = u >> 8;  // a part and its row's other parts lie in this bundle
+      part = (u >> 4) & 15;
+      parts = (u & 15) + 1;
+    }
+  } else if (s < a.nq) {
+    qb = a.nq - 1 - s;
   }
+  const bool active = qb >= 0;
+  const int qrow = active ? qb : 0;
   const size_t head_off = (size_t)bh * a.seqlen * D;
   const int bb = bh / a.heads, hq = bh - bb * a.heads;
   const size_t kv_off = (size_t)(bb * (a.heads / a.kv_group) + hq / a.kv_group) * a.seqlen * D;
@@ -1042,15 +1062,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const u32x4 rsk = buffer_resource(a.k + kv_off, kv_bytes), rsv = buffer_resource(a.v + kv_off, kv_bytes);
 
   QRegs<D> qf;
-  load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * qb + i) * D, h);
+  load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * qrow + i) * D, h);
 
-  // the row's bitmask
-  MaskWalk walk{0u, 0u, 0, (qb >> 5) + 1, 0u};
-  {
+  // the unit's bitmask
+  MaskWalk walk{0u, 0u, 0, (qrow >> 5) + 1, 0u};
+  if (active) {
     const int row = bh * a.nq + qb;
     int64_t e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
     e0 = e0 < 0 ? 0 : (e0 > a.col_cap ? a.col_cap : e0);
     e1 = e1 < e0 ? e0 : (e1 > a.col_cap ? a.col_cap : e1);
+    if (parts > 1) {  // this part's share of the row's entries
+      const int64_t n = e1 - e0;
+      const int64_t s0 = e0 + n * part / parts, s1 = e0 + n * (part + 1) / parts;
+      e0 = s0;
+      e1 = s1;
+    }
     for (int64_t base = e0; base < e1; base += 64) {
       int b = base + lane < e1 ? a.col_idx[base + lane] : -1;
       b = b >= 0 && b <= qb ? b : -1;
@@ -1068,8 +1094,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
       }
     }
-    walk.cur = walk.word(0);
   }
+  walk.cur = walk.word(0);
 
   // Copy x of a tile fills block x of its LDS layout (tile_offset): lane j
   // fetches row 16 (x % 2) + j / 4, chunk 4 (x / 2) + ((j % 4) ^ (j / 16 % 4)).
@@ -1090,7 +1116,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   vops.init(lane);
   RowState<D> st;
   st.init();
-  int c = walk.next();  // this step's block
+  int c = active ? walk.next() : -1;  // this step's block
   if (c >= 0) issue(c);
   // Q (loaded before the copies) and the first block in place.  Q then passes
   // through an empty asm statement, so that the compiler, which does not count
@@ -1112,14 +1138,78 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (c >= 0) wait_vm<0>();  // its copy has landed
   }
 
-  float* lse_out = a.lse != nullptr ? a.lse + (size_t)bh * a.seqlen + 32 * qb + i : nullptr;
-  finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
+  // Output.  Lane (i, h) holds O^T columns 32 t + 8 g + 4 h + e (t < D/32,
+  // g, e < 4) of query i: a whole row writes them normalised; the parts of a
+  // split row other than its first leave their normalised values (bf16) and
+  // log-sum-exp in their own slot, in the same order, for the first to merge.
+  const float l_tot = halves_sum(st.l);
+  const float lse2 = l_tot > 0.f ? st.m + __log2f(l_tot) : -INFINITY;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (active && parts == 1) {
+    float* lse_out = a.lse != nullptr ? a.lse + (size_t)bh * a.seqlen + 32 * qb + i : nullptr;
+    finish_rows<D>(st, a.o + head_off + (size_t)(32 * qb + i) * D, lse_out, h);
+  }
+  if (active && part > 0) {
+    bf16x4* po = reinterpret_cast<bf16x4*>(slot) + lane * (T::NT * 4);
+#pragma unroll
+    for (int t = 0; t < T::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.acc[t][4 * g + e] * inv);
+        po[4 * t + g] = w;
+      }
+    reinterpret_cast<float*>(slot + T::BYTES)[lane] = lse2;
+  }
+  __syncthreads();
+  if (active && parts > 1 && part == 0) {
+    float lp[kUnitBundle];
+    float m = lse2;
+#pragma unroll
+    for (int p = 1; p < kUnitBundle; ++p) {
+      lp[p] = p < parts ? reinterpret_cast<const float*>(slots[wave + p] + T::BYTES)[lane] : -INFINITY;
+      m = fmaxf(m, lp[p]);
+    }
+    // weights relative to the largest log-sum-exp (parts with no key weigh 0)
+    const float w0 = lse2 == -INFINITY ? 0.f : fast_exp2(lse2 - m);
+    float wsum = w0;
+#pragma unroll
+    for (int p = 1; p < kUnitBundle; ++p) {
+      lp[p] = lp[p] == -INFINITY ? 0.f : fast_exp2(lp[p] - m);
+      wsum += lp[p];
+    }
+    const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+    __bf16* orow = a.o + head_off + (size_t)(32 * qb + i) * D;
+#pragma unroll
+    for (int t = 0; t < T::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = w0 * st.acc[t][4 * g + e] * inv;
+#pragma unroll
+        for (int p = 1; p < kUnitBundle; ++p)
+          if (p < parts) {
+            const bf16x4 v = (reinterpret_cast<const bf16x4*>(slots[wave + p]) + lane * (T::NT * 4))[4 * t + g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] += lp[p] * (float)v[e];
+          }
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[e] * winv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * h) = w;
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[(size_t)bh * a.seqlen + 32 * qb + i] = wsum > 0.f ? (m + __log2f(wsum)) * kLn2 : -INFINITY;
+  }
 }
 
 template <int D>
 static void launch_rows(const AttnBf16Args& a, hipStream_t stream) {
   const int bhn = a.rows / a.nq;
-  const dim3 grid(8 * ((bhn + 7) / 8) * a.nq), block(64);
+  const int cap = a.plan != nullptr ? unit_slots(a.nq) : a.nq;
+  const dim3 grid(8 * ((bhn + 7) / 8) * ((cap + kUnitBundle - 1) / kUnitBundle)), block(64 * kUnitBundle);
   hipLaunchKernelGGL((attn_rows_kernel<D>), grid, block, 0, stream, a);
 }
 

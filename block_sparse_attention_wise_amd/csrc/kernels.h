@@ -18,7 +18,7 @@ struct AttnBf16Args {
   const int32_t* row_ptr;    // sparse kernel only
   const int32_t* col_idx;    // sparse kernel only
   int64_t col_cap;           // readable col_idx entries (<= INT32_MAX)
-  const int32_t* plan;       // sparse kernel: row order of wise_build_support ([rows]), or null
+  const int32_t* plan;       // sparse kernel: work units of wise_build_support, or null
   int seqlen;
   int nq;
   int rows;                  // batch * heads * nq
@@ -57,18 +57,26 @@ size_t support_workspace_bytes(int bh, int nq);
 // and its total size for bh rows of nq tiles
 __host__ __device__ constexpr int mass_ws_slot(int block) { return block == 16 ? 64 : 32; }
 size_t mass_ws_bytes(int64_t bh, int nq, int block);
-// entries of the schedule's row order: each head's query blocks, longest first
+// The schedule's work units for the bf16 sparse kernel (wise_build_support's
+// plan): per head a count, then unit_slots(nq) slots of units
+// (query block << 8) | (part << 4) | (parts - 1) or -1, run kUnitBundle to a
+// workgroup; a row splits in at most kUnitBundle parts, all in one bundle.
+constexpr int kUnitBundle = 4;
+__host__ __device__ constexpr int unit_slots(int nq) { return 4 * nq; }
+// resident row wavefronts of the sparse kernel per CU (two per SIMD)
+constexpr int kRowWavesPerCu = 8;
 size_t plan_capacity(int bh, int nq);
 // kind: 0 cumulative-eta support per step, unioned over the steps; 1 SizeMatched and
 // 2 MassMatched against the reference schedule (steps == 1)
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
                           const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream);
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, int row_slots, void* workspace,
+                          hipStream_t stream);
 // selection at block size 32 f (f = 2 or 4) on 32-token masses; the CSR and row order
 // stay at 32-token granularity
 size_t support_blocked_workspace_bytes(int bh, int nq, int steps, int f);
 hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, double eta, int f, int32_t* row_ptr,
-                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace,
+                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, int row_slots, void* workspace,
                                   hipStream_t stream);
 hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t* row_ptr, const int32_t* col_idx,
                                 int64_t cap, float* retained, hipStream_t stream);

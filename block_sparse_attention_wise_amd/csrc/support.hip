@@ -24,8 +24,8 @@
 //                 nnz.
 //   emit_csr      one wavefront per row: expands the bitmask into ascending
 //                 col_idx entries at row_ptr[row].
-//   order_rows    one workgroup per head: the head's query blocks, longest
-//                 scheduled row first (the sparse kernel's launch order).
+//   make_units    one workgroup per head: the head's work units for the sparse
+//                 kernel (rows, long rows split in parts), longest first.
 #include "common.h"
 #include "kernels.h"
 
@@ -315,45 +315,79 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
   }
 }
 
-// ---------------------------------------------------------------- row order
+// ---------------------------------------------------------------- work units
 //
-// The sparse kernel gives each query block (row) one wavefront that works
-// through the row's key blocks on its own, so a row's scheduled length is its
-// wavefront's serial work and the kernel ends after its longest rows do.  The
-// schedule's row order lists each head's query blocks by scheduled length,
-// longest first (ties: lower index first); the kernel starts rows in that order
-// so that the longest ones start first.  It only changes which rows run when.
+// The sparse kernel runs work units, one wavefront each, in bundles of
+// kUnitBundle wavefronts per workgroup; a wavefront walks its unit's key blocks
+// on its own, so a unit's block count is its serial work, and the kernel cannot
+// end before its longest unit does.  A unit is a whole query-block row, or one
+// of P near-equal contiguous parts of a row's CSR entries (part p takes entries
+// n p / P .. n (p+1) / P - 1 of its n) when the row is longer than the unit
+// length L: P = 2 for n <= 2 L, else 4.  L is the schedule's scheduled blocks
+// per resident row wavefront of the GPU (row_slots), so that no unit outlasts
+// the average slot's work, and at least the head's mean row length and
+// kUnitMin blocks.  A split row's parts share a bundle, which merges them from
+// LDS at its end.  A head's slots list the units of 4-part rows first (a bundle
+// each), then those of 2-part rows (two rows per bundle), then whole rows, each
+// class by unit length descending (ties: lower query block, then lower part):
+// the split classes' units are at most L long and the whole rows' at most L,
+// and within a class the longest start first.  Splitting only reorders
+// floating-point sums.
 constexpr int kOrderThreads = 256;
-constexpr int kRankSortMax = 1024;  // rows sorted by rank (else bitonic)
-static_assert(kMaxNq <= 4096, "12-bit row index in the sort key");
+constexpr int kUnitMin = 4;
+static_assert(kMaxNq <= 4096 && kUnitBundle == 4, "unit sort key: class, 13-bit length, 12-bit row, 2-bit part");
 
-__global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(const int32_t* counts, int nq, int32_t* order) {
-  __shared__ uint32_t keys[kMaxNq];
-  __shared__ uint32_t sorted[kRankSortMax];
-  const int h = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ int unit_parts(int n, int len) { return n <= len ? 1 : (n <= 2 * len ? 2 : 4); }
+
+__global__ __launch_bounds__(kOrderThreads) void make_units_kernel(const int32_t* counts, int nq, int bh,
+                                                                   const int32_t* nnz, int row_slots,
+                                                                   int32_t* plan) {
+  extern __shared__ uint32_t keys[];  // unit_slots(nq) keys
+  __shared__ int32_t part_sum[kOrderThreads / 64];
+  __shared__ int32_t wave_units[kOrderThreads / 64];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cap = unit_slots(nq);
   const int32_t* cnt = counts + (size_t)h * nq;
-  // sort keys (count descending, row ascending; all distinct): up to
-  // kRankSortMax rows each key goes to its rank, the number of smaller keys
-  // (broadcast LDS reads, no barrier per pass); beyond, bitonic over a power of two
-  int n2 = 1;
-  while (n2 < nq) n2 <<= 1;
-  for (int q = tid; q < n2; q += kOrderThreads) {
-    const int c = q < nq ? min(max(cnt[q], 0), nq) : 0;
-    keys[q] = q < nq ? ((uint32_t)(kMaxNq - c) << 12) | (uint32_t)q : 0xFFFFFFFFu;
-  }
+  const int per = (nq + kOrderThreads - 1) / kOrderThreads;  // rows per thread, contiguous
+  const int r0 = min(nq, tid * per), r1 = min(nq, r0 + per);
+  // the head's scheduled blocks
+  int local = 0;
+  for (int r = r0; r < r1; ++r) local += min(max(cnt[r], 0), nq);
+  for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
+  if (lane == 0) part_sum[w] = local;
   __syncthreads();
-  if (nq <= kRankSortMax) {
-    for (int q = tid; q < nq; q += kOrderThreads) {
-      const uint32_t kq = keys[q];
-      int rank = 0;
-#pragma unroll 8
-      for (int p = 0; p < nq; ++p) rank += keys[p] < kq ? 1 : 0;
-      sorted[rank] = kq;
-    }
-    __syncthreads();
-    for (int q = tid; q < nq; q += kOrderThreads) order[(size_t)h * nq + q] = (int32_t)(sorted[q] & 0xFFFu);
-    return;
+  int head_total = 0;
+  for (int k = 0; k < kOrderThreads / 64; ++k) head_total += part_sum[k];
+  const int64_t total = max(*nnz, 0);
+  const int slots = max(row_slots, 1);
+  const int len = max(max(kUnitMin, (int)((total + slots - 1) / slots)), (head_total + nq - 1) / nq);
+  // this thread's units, then an exclusive scan over the threads
+  int mine = 0;
+  for (int r = r0; r < r1; ++r) mine += unit_parts(min(max(cnt[r], 0), nq), len);
+  int inc = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
   }
+  if (lane == 63) wave_units[w] = inc;
+  __syncthreads();
+  int at = inc - mine;
+  for (int k = 0; k < w; ++k) at += wave_units[k];
+  int units = 0;
+  for (int k = 0; k < kOrderThreads / 64; ++k) units += wave_units[k];
+  // sort keys (class: 4 parts, 2 parts, whole; unit length descending; row,
+  // part ascending; all distinct)
+  for (int r = r0; r < r1; ++r) {
+    const int n = min(max(cnt[r], 0), nq), parts = unit_parts(n, len);
+    const uint32_t cls = parts == 4 ? 0u : (parts == 2 ? 1u : 2u);
+    const int ul = (n + parts - 1) / parts;
+    for (int p = 0; p < parts; ++p)
+      keys[at++] = (cls << 29) | ((uint32_t)(kMaxNq - ul) << 14) | ((uint32_t)r << 2) | (uint32_t)p;
+  }
+  int n2 = 1;
+  while (n2 < units) n2 <<= 1;
+  for (int x = units + tid; x < n2; x += kOrderThreads) keys[x] = 0xFFFFFFFFu;
+  __syncthreads();
   for (int k = 2; k <= n2; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < n2; i += kOrderThreads) {
@@ -368,10 +402,25 @@ __global__ __launch_bounds__(kOrderThreads) void order_rows_kernel(const int32_t
       }
       __syncthreads();
     }
-  for (int q = tid; q < nq; q += kOrderThreads) order[(size_t)h * nq + q] = (int32_t)(keys[q] & 0xFFFu);
+  // sorted order = slot order: 4-part rows fill whole bundles (their count is a
+  // multiple of 4), 2-part rows start at even slots; plan[h] = the head's unit
+  // count, its units at plan[bh + h * unit_slots(nq) ..]:
+  // (query block << 8) | (part << 4) | (parts - 1), -1 past the count
+  if (tid == 0) plan[h] = units;
+  int32_t* out = plan + bh + (size_t)h * cap;
+  for (int x = tid; x < cap; x += kOrderThreads) {
+    if (x < units) {
+      const uint32_t key = keys[x];
+      const int r = (int)((key >> 2) & 0xFFFu), p = (int)(key & 3u);
+      const int parts = unit_parts(min(max(cnt[r], 0), nq), len);
+      out[x] = (r << 8) | (p << 4) | (parts - 1);
+    } else {
+      out[x] = -1;
+    }
+  }
 }
 
-size_t plan_capacity(int bh, int nq) { return (size_t)bh * nq; }
+size_t plan_capacity(int bh, int nq) { return (size_t)bh + (size_t)bh * unit_slots(nq); }
 
 size_t support_workspace_bytes(int bh, int nq) {
   const size_t rows = (size_t)bh * nq;
@@ -417,10 +466,10 @@ hipError_t launch_retained_mass(const float* mass, int bh, int nq, const int32_t
   return hipGetLastError();
 }
 
-// CSR (row_ptr, col_idx, nnz) and, if plan != null, the row order from the
+// CSR (row_ptr, col_idx, nnz) and, if plan != null, the work units from the
 // per-row bitmasks and counts in the workspace
 static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz, int32_t* plan,
-                                  void* workspace, hipStream_t stream) {
+                                  int row_slots, void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -434,13 +483,15 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   hipLaunchKernelGGL(emit_csr_kernel, dim3((unsigned)rows), dim3(64), 0, stream, masks, nwords, row_ptr, col_idx);
   e = hipGetLastError();
   if (e != hipSuccess || plan == nullptr) return e;
-  hipLaunchKernelGGL(order_rows_kernel, dim3(bh), dim3(kOrderThreads), 0, stream, counts, nq, plan);
+  hipLaunchKernelGGL(make_units_kernel, dim3(bh), dim3(kOrderThreads), (size_t)unit_slots(nq) * sizeof(uint32_t),
+                     stream, counts, nq, bh, nnz, row_slots, plan);
   return hipGetLastError();
 }
 
 hipError_t launch_support(const float* mass, int bh, int nq, int steps, double eta, int kind,
                           const int32_t* ref_row_ptr, const int32_t* ref_col_idx, int64_t ref_cap, int32_t* row_ptr,
-                          int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace, hipStream_t stream) {
+                          int32_t* col_idx, int32_t* nnz, int32_t* plan, int row_slots, void* workspace,
+                          hipStream_t stream) {
   const size_t rows = (size_t)bh * nq;
   const int nwords = (nq + 31) / 32;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -460,7 +511,7 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, row_slots, workspace, stream);
 }
 
 // ---------------------------------------------------------------- coarser blocks
@@ -520,7 +571,7 @@ size_t support_blocked_workspace_bytes(int bh, int nq, int steps, int f) {
 }
 
 hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, double eta, int f, int32_t* row_ptr,
-                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, void* workspace,
+                                  int32_t* col_idx, int32_t* nnz, int32_t* plan, int row_slots, void* workspace,
                                   hipStream_t stream) {
   const int nqb = nq / f;
   const int nwb = (nqb + 31) / 32;
@@ -558,7 +609,7 @@ hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, 
                      masks, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, workspace, stream);
+  return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, row_slots, workspace, stream);
 }
 
 }  // namespace wise

@@ -38,6 +38,15 @@ wise_status check_attn_shape(wise_dtype dt, int batch, int heads, int kv_heads, 
   return WISE_OK;
 }
 
+// resident row wavefronts of the bf16 sparse kernel on the current device
+int sparse_row_slots() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256 * kRowWavesPerCu;
+  return cus * kRowWavesPerCu;
+}
+
 float resolve_scale(float scale, int head_dim) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim); }
 
 wise_status run_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen, int head_dim, int block,
@@ -180,7 +189,7 @@ wise_status wise_build_support(int bh, int nq, int num_steps, const float* mass,
   if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support(mass, bh, nq, num_steps, (double)eta, 0, nullptr, nullptr, 0, row_ptr, col_idx, nnz,
-                                plan, workspace, static_cast<hipStream_t>(stream));
+                                plan, sparse_row_slots(), workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -223,7 +232,7 @@ wise_status wise_build_support_blocked(int block, int bh, int nq, int num_steps,
   if (st != WISE_OK) return st;
   if (!(eta > 0.f) || !(eta <= 1.f)) return WISE_ERR_INVALID_ARG;
   hipError_t e = launch_support_blocked(mass, bh, nq, num_steps, (double)eta, f, row_ptr, col_idx, nnz, plan,
-                                        workspace, static_cast<hipStream_t>(stream));
+                                        sparse_row_slots(), workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -255,7 +264,7 @@ wise_status wise_build_support_variant(wise_support_variant kind, int bh, int nq
     if (!aligned4(ref_row_ptr) || !aligned4(ref_col_idx)) return WISE_ERR_INVALID_ARG;
   }
   hipError_t e = launch_support(mass, bh, nq, 1, (double)eta, k, ref_row_ptr, ref_col_idx, ref_col_capacity, row_ptr,
-                                col_idx, nnz, plan, workspace, static_cast<hipStream_t>(stream));
+                                col_idx, nnz, plan, sparse_row_slots(), workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WISE_OK : WISE_ERR_HIP;
 }
 
@@ -281,7 +290,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
   // 16-token rows are bitmasks of 2048 blocks in both kernels' LDS
   if (block != kBlock && seqlen / block > kMaxSparseBlocks16) return WISE_ERR_UNSUPPORTED;
   if (plan != nullptr) {
-    // the row order holds one entry per row
+    // every unit slot of every head must be readable
     const int64_t bh = (int64_t)batch * heads;
     const size_t need = bh <= INT32_MAX ? wise_build_support_plan_capacity((int)bh, seqlen / kBlock) : 0;
     if (!aligned4(plan) || need == 0 || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;

@@ -19,7 +19,7 @@ WISE_OK, WISE_ERR_INVALID_ARG, WISE_ERR_UNSUPPORTED, WISE_ERR_HIP = 0, 1, 2, 3
 WISE_BF16, WISE_FP32 = 0, 1
 BLOCK = 32
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 EXPORTED = (
     "wise_abi_version", "wise_status_string", "wise_full_attn_mass", "wise_full_attn_mass_workspace_bytes",
     "wise_dense_attn",
@@ -211,8 +211,7 @@ def build_support_plan_capacity(bh: int, nq: int) -> int:
 
 class Schedule:
     """Device-resident CSR schedule: row_ptr [rows+1], col_idx [capacity], nnz [1] (int32),
-    and optionally its row order (int32 [rows]: each head's query blocks, longest
-    scheduled row first), or None."""
+    and optionally its work units for the bf16 sparse kernel (int32, or None)."""
 
     def __init__(self, row_ptr, col_idx, nnz, bh, nq, plan=None):
         self.row_ptr, self.col_idx, self.nnz, self.bh, self.nq = row_ptr, col_idx, nnz, bh, nq
@@ -333,9 +332,9 @@ def retained_mass(mass, schedule: Schedule, *, out=None, stream=None):
 
 def sparse_attn(q, k, v, schedule: Schedule, *, out=None, lse=None, want_lse=False, scale=None,
                 block=BLOCK, stream=None):
-    """Block-sparse causal attention over a CSR schedule (starting rows in its row order
-    when it carries one).  block 16 takes a 16-token schedule (build_support on 16-token
-    masses; no row order).  Returns (out, lse)."""
+    """Block-sparse causal attention over a CSR schedule (running its work units when it
+    carries them).  block 16 takes a 16-token schedule (build_support on 16-token
+    masses; no units).  Returns (out, lse)."""
     b, h, hk, n, d = _qkv_shape(q, k, v)
     out = _out_like(q, out)
     if want_lse and lse is None:

@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 10
+#define WISE_ABI_VERSION 11
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -116,8 +116,9 @@ wise_status wise_dense_attn(wise_dtype dt, int batch, int heads, int kv_heads, i
 size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
 
 /*
- * int32 entries of the optional row order wise_build_support can emit beside
- * the CSR schedule for bh rows of nq query blocks: bh * nq (0 on invalid sizes).
+ * int32 entries of the optional work-unit list wise_build_support can emit
+ * beside the CSR schedule for bh rows of nq query blocks: bh + bh * 4 * nq
+ * (0 on invalid sizes).
  */
 size_t wise_build_support_plan_capacity(int bh, int nq);
 
@@ -140,14 +141,25 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *   col_idx     : int32 [col_capacity], written; ascending within a row.
  *   col_capacity: must be >= bh*nq*(nq+1)/2 (the fully dense worst case).
  *   nnz         : int32 device scalar, written with row_ptr[bh*nq].
- *   plan        : NULL, or int32 [plan_capacity] receiving the row order of the
- *                 same schedule (the execution metadata the WISE paper, App. B,
- *                 prepares with the sparse schedule), with
- *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq):
- *                 plan[bh_index*nq + j], j = 0 .. nq-1, lists the query blocks
- *                 of (batch, head) bh_index in order of scheduled block count,
- *                 longest first (ties: lower index first) -- a permutation of
- *                 0 .. nq-1, the order the bf16 sparse kernel starts its rows in.
+ *   plan        : NULL, or int32 [plan_capacity] receiving the work units of
+ *                 the same schedule for the bf16 sparse kernel (the execution
+ *                 metadata the WISE paper, App. B, prepares with the sparse
+ *                 schedule), with
+ *                 plan_capacity >= wise_build_support_plan_capacity(bh, nq).
+ *                 A unit is one query block's row, or one of P near-equal
+ *                 contiguous parts of its CSR entries (part p takes entries
+ *                 n*p/P .. n*(p+1)/P - 1 of its n) when n exceeds the unit
+ *                 length L = max(4, ceil(nnz / S), ceil(n_head / nq)), S the
+ *                 resident row wavefronts of the current device (8 per CU) and
+ *                 n_head the head's scheduled blocks: P = 2 for n <= 2L, else 4.
+ *                 The kernel runs units four to a workgroup, a split row's
+ *                 parts in one.  plan[h] (h < bh) is head h's unit count U_h,
+ *                 and plan[bh + h*4*nq + j] for j < U_h its units,
+ *                 (query block << 8) | (part << 4) | (P - 1), in the order: the
+ *                 units of 4-part rows, then of 2-part rows, then whole rows,
+ *                 each class by ceil(n / P) descending, then query block, then
+ *                 part (so a 4-part row fills slots 4k .. 4k+3 and a 2-part row
+ *                 starts at an even slot); -1 for j >= U_h.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.
@@ -265,25 +277,29 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  *                            kernels mask the unscheduled 16 x 16 sub-blocks of the
  *                            32 x 32 tiles they visit.
  *   col_capacity           : number of readable col_idx entries.
- *   plan, plan_capacity    : NULL, or the row order wise_build_support wrote for
- *                            this same schedule, plan_capacity its readable int32
- *                            entries (at least
+ *   plan, plan_capacity    : NULL, or the work units wise_build_support wrote
+ *                            for this same schedule, plan_capacity its readable
+ *                            int32 entries (at least
  *                            wise_build_support_plan_capacity(batch*heads,
  *                            seqlen / 32), else WISE_ERR_INVALID_ARG).  The bf16
- *                            kernel at block 32 gives every query block one
- *                            wavefront of its own, which walks the block's CSR
- *                            row; with a row order it starts each head's rows
- *                            in that order (longest first), without one in
- *                            descending query-block order.  The results do not
- *                            depend on it; the fp32 kernel and block 16 ignore it.
+ *                            kernel at block 32 gives every unit (without units:
+ *                            every query block's row) one wavefront of its own,
+ *                            which walks the unit's CSR entries, four units to a
+ *                            workgroup in the listed order (without units, in
+ *                            descending query-block order); the parts of a split
+ *                            row are merged exactly (weights 2^(L_p - L) of the
+ *                            parts' log-sum-exps) in their workgroup, so the
+ *                            results only differ in floating-point summation
+ *                            order.  The fp32 kernel and block 16 ignore it.
  * Entries outside 0..q and CSR offsets outside 0..col_capacity are ignored
- * (clamped); a block listed twice counts once.  A row order must be a
- * permutation of each head's query blocks, as wise_build_support writes it
- * (entries outside 0..nq-1 are skipped, and a row it does not list is not
- * computed).  A row left with no admissible key writes o = 0 and lse = -inf
- * (wise_build_support never produces one).  Both kernels support up to 4096 key
- * blocks per head (seqlen <= 131072), and up to 2048 at block 16
- * (seqlen <= 32768); beyond that WISE_ERR_UNSUPPORTED is returned.
+ * (clamped); without work units a block listed twice counts once.  Work units
+ * must be wise_build_support's for this same schedule: their parts split the
+ * CSR rows it writes (ascending, each block once), and a row they do not list
+ * is not computed (units naming no row, or parts not within one workgroup's
+ * four slots, are skipped).  A row left with no admissible key writes o = 0
+ * and lse = -inf (wise_build_support never produces one).  Both kernels
+ * support up to 4096 key blocks per head (seqlen <= 131072), and up to 2048 at
+ * block 16 (seqlen <= 32768); beyond that WISE_ERR_UNSUPPORTED is returned.
  */
 wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, int seqlen,
                              int head_dim, int block, const void* q, const void* k, const void* v, void* o,

@@ -69,7 +69,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 10
+    assert lib.wise_abi_version() == 11
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"
@@ -141,9 +141,9 @@ def test_workspace_bytes(lib):
 def test_plan_capacity(lib):
     f = lib.wise_build_support_plan_capacity
     assert f(0, 8) == 0 and f(1, 0) == 0 and f(1, 4097) == 0
-    # one row-order entry per (head, query block)
+    # a unit count per head, then 4 nq unit slots per head
     for bh, nq in ((1, 8), (32, 128), (3, 33), (1, 1)):
-        assert f(bh, nq) == bh * nq
+        assert f(bh, nq) == bh + bh * 4 * nq
 
 
 def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0,
@@ -192,9 +192,9 @@ def test_sparse_validation(lib):
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
     assert sp(d=80) == UNSUPPORTED
-    need = lib.wise_build_support_plan_capacity(1, 4)    # one row-order entry per query block
-    assert need == 4
-    assert sp(plan=P, pcap=need - 1) == INVALID         # a row would be out of reach
+    need = lib.wise_build_support_plan_capacity(1, 4)    # a count and 16 unit slots
+    assert need == 1 + 16
+    assert sp(plan=P, pcap=need - 1) == INVALID         # a unit slot would be out of reach
     assert sp(plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
 
 

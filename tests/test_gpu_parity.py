@@ -362,13 +362,31 @@ def test_uniform_attention_closed_form_on_gpu():
     assert_mass_close(f64(mass[0]), O.block_mass(np.zeros((n, d)), f64(k[0, 0])), "bf16", "uniform mass")
 
 
+def _expected_units(counts, nq, nnz, slots):
+    """The work units of wise_build_support, on the host, for one head: unit
+    length L = max(4, ceil(nnz / slots), ceil(head blocks / nq)); a row of n > L
+    blocks splits in P = 2 parts (n <= 2 L) or 4; units of 4-part rows, then
+    2-part rows, then whole rows, each by ceil(n / P) descending, then row, then
+    part; encoded (row << 8) | (part << 4) | (P - 1)."""
+    length = max(4, -(-nnz // slots), -(-sum(counts) // nq))
+    units = []
+    for r, n in enumerate(counts):
+        parts = 1 if n <= length else (2 if n <= 2 * length else 4)
+        ul = -(-n // parts)
+        cls = {4: 0, 2: 1, 1: 2}[parts]
+        units += [(cls, -ul, r, p, parts) for p in range(parts)]
+    units.sort()
+    return [(r << 8) | (p << 4) | (parts - 1) for _, _, r, p, parts in units]
+
+
 @pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0), (1, 300, 0.99),
                                        (2, 64, 0.9), (11, 16, 0.9), (1, 1100, 0.95)])
-def test_row_order_is_longest_first(bh, nq, eta):
-    """The schedule's row order lists each head's query blocks once, by scheduled
-    block count (longest first, lower index first); rank sort up to 1024 rows,
-    bitonic beyond (nq = 1100).  The sparse kernel gives the same rows through the
-    row order as without it (descending query blocks), and the oracle's values."""
+def test_work_units_split_long_rows(bh, nq, eta):
+    """The schedule's work units: per head a count, then its rows (longer rows
+    split in parts of their CSR entries) longest first -- the rule written out on
+    the host, bitonic-sorted on the GPU up to 2 nq units.  Sparse attention
+    through the units (split rows merged from their parts) gives the oracle's
+    values, and the same values as without units up to summation order."""
     wise = _wise()
     rng = np.random.default_rng(bh * 1000 + nq)
     m = np.zeros((4, bh, nq, nq), dtype=np.float32)
@@ -376,11 +394,11 @@ def test_row_order_is_longest_first(bh, nq, eta):
         for r in range(bh):
             for qb in range(nq):
                 m[s, r, qb, :qb + 1] = rng.dirichlet(np.full(qb + 1, 0.4))
-    note(f"row order bh={bh} nq={nq} eta={eta}")
+    note(f"work units bh={bh} nq={nq} eta={eta}")
     sched = wise.build_support(torch.from_numpy(m).to(DEV), eta)
     torch.cuda.synchronize()
-    assert sched.plan is not None and sched.plan.numel() == bh * nq
-    order = sched.plan.cpu().numpy().reshape(bh, nq)
+    assert sched.plan is not None and sched.plan.numel() == bh + bh * 4 * nq
+    plan = sched.plan.cpu().numpy()
     gpu_rows = csr_rows(sched.row_ptr, sched.col_idx)
     ref_rows, flags = [], []
     for r in range(bh):
@@ -390,32 +408,55 @@ def test_row_order_is_longest_first(bh, nq, eta):
             flags.append(fl)
     bad, _ = compare_supports(gpu_rows, ref_rows, flags)
     assert not bad
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * 8
+    nnz = int(sched.nnz.item())
+    split = 0
     for h in range(bh):
         counts = [len(gpu_rows[h * nq + q]) for q in range(nq)]
-        want = sorted(range(nq), key=lambda q: (-counts[q], q))
-        assert order[h].tolist() == want, f"head {h}: row order"
+        want = _expected_units(counts, nq, nnz, slots)
+        got = plan[bh + h * 4 * nq:bh + (h + 1) * 4 * nq]
+        assert int(plan[h]) == len(want) <= 4 * nq, f"head {h}: unit count"
+        assert got[:len(want)].tolist() == want, f"head {h}: units"
+        assert np.all(got[len(want):] == -1)
+        split += sum(1 for u in want if (u & 15) > 0)
+    # cover the split path: a schedule whose units include split rows ...
+    n, d = 32 * nq, 128
     if nq > 300:
         return
-    # sparse attention through the row order vs without it vs the oracle
-    n, d = 32 * nq, 128
     q, k, v = (torch.from_numpy(rng.standard_normal((1, bh, n, d)).astype(np.float32)).to(torch.bfloat16)
                for _ in range(3))
     dq, dk, dv = q.to(DEV), k.to(DEV), v.to(DEV)
     op, lp = wise.sparse_attn(dq, dk, dv, sched, want_lse=True)
     csr_only = wise.Schedule(sched.row_ptr, sched.col_idx, sched.nnz, bh, nq)
     oc, lc = wise.sparse_attn(dq, dk, dv, csr_only, want_lse=True)
+    # ... and the same schedule with every row forced into 4 parts (hand-made units,
+    # one workgroup per row; rows with fewer than 4 blocks leave parts empty:
+    # log-sum-exp -inf, weight 0)
+    forced = np.full(bh + bh * 4 * nq, -1, dtype=np.int32)
+    for h in range(bh):
+        forced[h] = 4 * nq
+        forced[bh + h * 4 * nq:bh + (h + 1) * 4 * nq] = [(qb << 8) | (p << 4) | 3 for qb in range(nq)
+                                                        for p in range(4)]
+    rows_forced = set(range(nq))
+    fsched = wise.Schedule(sched.row_ptr, sched.col_idx, sched.nnz, bh, nq, plan=torch.from_numpy(forced).to(DEV))
+    of, lf = wise.sparse_attn(dq, dk, dv, fsched, want_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(op, oc), "row order changed the values"
-    assert torch.equal(lp, lc)
+    assert_attn_close(f64(op), f64(oc), "bf16", "units vs CSR O")
+    assert float((lp - lc).abs().max()) <= 1e-5
     for h in range(bh):
         rows_h = ref_rows[h * nq:(h + 1) * nq]
         ro, rl = O.sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), rows_h)
         keep = np.zeros(n, dtype=bool)
+        kf = np.zeros(n, dtype=bool)
         for qb in range(nq):
             if set(gpu_rows[h * nq + qb].tolist()) == set(rows_h[qb].tolist()):
                 keep[32 * qb:32 * qb + 32] = True
-        assert_attn_close(f64(op[0, h])[keep], ro[keep], "bf16", f"row order head {h} O")
-        assert_lse_close(f64(lp[0, h])[keep], rl[keep], "bf16", f"row order head {h}")
+                kf[32 * qb:32 * qb + 32] = qb in rows_forced
+        assert_attn_close(f64(op[0, h])[keep], ro[keep], "bf16", f"units head {h} O")
+        assert_lse_close(f64(lp[0, h])[keep], rl[keep], "bf16", f"units head {h}")
+        assert_attn_close(f64(of[0, h])[kf], ro[kf], "bf16", f"4-part rows head {h} O")
+        assert_lse_close(f64(lf[0, h])[kf], rl[kf], "bf16", f"4-part rows head {h}")
+    record(f"work units bh={bh} nq={nq} eta={eta}", rows=bh * nq, split_parts=split)
 
 
 def test_high_dynamic_range_logits():
