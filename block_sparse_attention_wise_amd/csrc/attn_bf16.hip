@@ -1014,11 +1014,14 @@ __global__ __launch_bounds__(64 * kUnitBundle) __attribute__((amdgpu_waves_per_e
   const int i = lane & 31, h = lane >> 5;
   unsigned char* const slot = slots[wave];
   const int bhn = a.rows / a.nq;
-  // bundle r of a head: its unit slots kUnitBundle r .. kUnitBundle r + 3 (the
-  // units longest first within their split class), or without units query
-  // blocks nq - 1 - kUnitBundle r - w (later rows tend to be longer)
+  // Workgroup r of a head runs its bundles r, r + G, r + 2 G, ... (G =
+  // ceil(nq / kUnitBundle) workgroups per head, enough for the head's whole
+  // rows; split rows add bundles past G): bundle b holds the unit slots
+  // kUnitBundle b .. kUnitBundle b + 3 (the units longest first within their
+  // split class), or without units query blocks nq - 1 - kUnitBundle b - w
+  // (later rows tend to be longer).
   const int cap = a.plan != nullptr ? unit_slots(a.nq) : a.nq;
-  const int per_head = (cap + kUnitBundle - 1) / kUnitBundle;
+  const int per_head = (a.nq + kUnitBundle - 1) / kUnitBundle;
   // XCD-aligned head runs taken hg heads at a time, as in the streaming kernel,
   // hg the fewest heads whose rows fill the XCD's wavefront slots twice over: a
   // unit is one wavefront's serial work, so the longest units of all the heads
@@ -1037,46 +1040,76 @@ __global__ __launch_bounds__(64 * kUnitBundle) __attribute__((amdgpu_waves_per_e
     bh = start + c * hg + within % hc;
     rank = within / hc;
   }
-  // this wavefront's unit: query block qb, part `part` of `parts` (qb < 0: none)
-  const int s = kUnitBundle * rank + wave;
-  int qb = -1, part = 0, parts = 1;
-  if (a.plan != nullptr) {
-    const int units = min(a.plan[bh], cap);
-    if (kUnitBundle * rank >= units) return;  // an empty bundle (uniform over the workgroup)
-    const int u = s < units ? a.plan[bhn + (size_t)bh * cap + s] : -1;
-    if (u >= 0 && (u >> 8) < a.nq && ((u >> 4) & 15) < (u & 15) + 1 && (u & 15) < kUnitBundle &&
-        wave - ((u >> 4) & 15) >= 0 && wave - ((u >> 4) & 15) + (u & 15) < kUnitBundle) {
-      qb = u >> 8;  // a part and its row's other parts lie in this bundle
-      part = (u >> 4) & 15;
-      parts = (u & 15) + 1;
-    }
-  } else if (s < a.nq) {
-    qb = a.nq - 1 - s;
-  }
-  const bool active = qb >= 0;
-  const int qrow = active ? qb : 0;
   const size_t head_off = (size_t)bh * a.seqlen * D;
   const int bb = bh / a.heads, hq = bh - bb * a.heads;
   const size_t kv_off = (size_t)(bb * (a.heads / a.kv_group) + hq / a.kv_group) * a.seqlen * D;
   const uint32_t kv_bytes = (uint32_t)a.seqlen * (uint32_t)(D * 2);
   const u32x4 rsk = buffer_resource(a.k + kv_off, kv_bytes), rsv = buffer_resource(a.v + kv_off, kv_bytes);
+  KOps kops;
+  kops.init(i, h);
+  VOps vops;
+  vops.init(lane);
+  for (int bundle = rank;; bundle += per_head) {
+  // this wavefront's unit: query block qb, part `part` of `parts` (qb < 0: none),
+  // its CSR entries [e0, e1) and their first key block
+  const int s = kUnitBundle * bundle + wave;
+  if (kUnitBundle * bundle >= cap) break;  // uniform over the workgroup
+  int qb = -1, part = 0, parts = 1, first = -1;
+  int64_t e0 = 0, e1 = 0;
+  if (a.plan != nullptr) {
+    // this slot's unit (in bounds: s < cap) and the head's unit count load
+    // together, and every field is decoded before the first branch
+    const int4 ue = reinterpret_cast<const int4*>(a.plan + unit_base(bhn))[(size_t)bh * cap + s];
+    const int units = min(a.plan[bh], cap);
+    const int u = s < units ? ue.x : -1;
+    const int up = (u >> 4) & 15, un = (u & 15) + 1;
+    // a part and its row's other parts lie in this bundle
+    const bool ok = u >= 0 && (u >> 8) < a.nq && up < un && un <= kUnitBundle && wave - up >= 0 &&
+                    wave - up + un <= kUnitBundle;
+    const int64_t f0 = ue.y < 0 ? 0 : (ue.y > a.col_cap ? a.col_cap : ue.y);
+    const int64_t f1 = ue.z < f0 ? f0 : (ue.z > a.col_cap ? a.col_cap : ue.z);
+    qb = ok ? u >> 8 : -1;
+    part = ok ? up : 0;
+    parts = ok ? un : 1;
+    e0 = ok ? f0 : 0;
+    e1 = ok ? f1 : 0;
+    first = ok ? ue.w : -1;
+    if (kUnitBundle * bundle >= units) break;  // past the head's units (uniform over the workgroup)
+  } else if (s < a.nq) {
+    qb = a.nq - 1 - s;
+    const int row = bh * a.nq + qb;
+    e0 = a.row_ptr[row];
+    e1 = a.row_ptr[row + 1];
+    e0 = e0 < 0 ? 0 : (e0 > a.col_cap ? a.col_cap : e0);
+    e1 = e1 < e0 ? e0 : (e1 > a.col_cap ? a.col_cap : e1);
+  }
+  const bool active = qb >= 0;
+  const int qrow = active ? qb : 0;
 
   QRegs<D> qf;
   load_frag<D>(qf.f, a.q + head_off + (size_t)(32 * qrow + i) * D, h);
 
+  // Copy x of a tile fills block x of its LDS layout (tile_offset): lane j
+  // fetches row 16 (x % 2) + j / 4, chunk 4 (x / 2) + ((j % 4) ^ (j / 16 % 4)).
+  const uint32_t lane_src = (uint32_t)((lane >> 2) * (2 * D) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const uint32_t lb = lds_address(slot);
+  auto issue = [&](int b) {
+    const uint32_t tile = (uint32_t)b * (uint32_t)T::BYTES;
+#pragma unroll
+    for (int x = 0; x < CI; ++x)
+      copy_to_lds(rsk, lb + 1024 * x, lane_src, tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64));
+#pragma unroll
+    for (int x = 0; x < CI; ++x)
+      copy_to_lds(rsv, lb + T::BYTES + 1024 * x, lane_src, tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64));
+  };
+  // the unit's first block (from the unit list) starts copying now, beside the
+  // loads of Q and of the unit's CSR entries
+  const bool pre = active && first >= 0 && first <= qb;
+  if (pre) issue(first);
+
   // the unit's bitmask
   MaskWalk walk{0u, 0u, 0, (qrow >> 5) + 1, 0u};
   if (active) {
-    const int row = bh * a.nq + qb;
-    int64_t e0 = a.row_ptr[row], e1 = a.row_ptr[row + 1];
-    e0 = e0 < 0 ? 0 : (e0 > a.col_cap ? a.col_cap : e0);
-    e1 = e1 < e0 ? e0 : (e1 > a.col_cap ? a.col_cap : e1);
-    if (parts > 1) {  // this part's share of the row's entries
-      const int64_t n = e1 - e0;
-      const int64_t s0 = e0 + n * part / parts, s1 = e0 + n * (part + 1) / parts;
-      e0 = s0;
-      e1 = s1;
-    }
     for (int64_t base = e0; base < e1; base += 64) {
       int b = base + lane < e1 ? a.col_idx[base + lane] : -1;
       b = b >= 0 && b <= qb ? b : -1;
@@ -1097,27 +1130,13 @@ __global__ __launch_bounds__(64 * kUnitBundle) __attribute__((amdgpu_waves_per_e
   }
   walk.cur = walk.word(0);
 
-  // Copy x of a tile fills block x of its LDS layout (tile_offset): lane j
-  // fetches row 16 (x % 2) + j / 4, chunk 4 (x / 2) + ((j % 4) ^ (j / 16 % 4)).
-  const uint32_t lane_src = (uint32_t)((lane >> 2) * (2 * D) + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
-  const uint32_t lb = lds_address(slot);
-  auto issue = [&](int b) {
-    const uint32_t tile = (uint32_t)b * (uint32_t)T::BYTES;
-#pragma unroll
-    for (int x = 0; x < CI; ++x)
-      copy_to_lds(rsk, lb + 1024 * x, lane_src, tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64));
-#pragma unroll
-    for (int x = 0; x < CI; ++x)
-      copy_to_lds(rsv, lb + T::BYTES + 1024 * x, lane_src, tile + (uint32_t)((x & 1) * 32 * D + (x >> 1) * 64));
-  };
-  KOps kops;
-  kops.init(i, h);
-  VOps vops;
-  vops.init(lane);
   RowState<D> st;
   st.init();
   int c = active ? walk.next() : -1;  // this step's block
-  if (c >= 0) issue(c);
+  if (c >= 0 && !(pre && c == first)) {
+    if (pre) wait_vm<0>();  // a unit list that disagrees with its CSR: the copy already made is dropped
+    issue(c);
+  }
   // Q (loaded before the copies) and the first block in place.  Q then passes
   // through an empty asm statement, so that the compiler, which does not count
   // the copies, sees no load of Q outstanding in the loop and adds no vmcnt
@@ -1203,13 +1222,15 @@ __global__ __launch_bounds__(64 * kUnitBundle) __attribute__((amdgpu_waves_per_e
     if (a.lse != nullptr && h == 0)
       a.lse[(size_t)bh * a.seqlen + 32 * qb + i] = wsum > 0.f ? (m + __log2f(wsum)) * kLn2 : -INFINITY;
   }
+  if (a.plan == nullptr) break;  // without units a head has no bundles past G
+  __syncthreads();  // the merge read the slots the next bundle's copies refill
+  }
 }
 
 template <int D>
 static void launch_rows(const AttnBf16Args& a, hipStream_t stream) {
   const int bhn = a.rows / a.nq;
-  const int cap = a.plan != nullptr ? unit_slots(a.nq) : a.nq;
-  const dim3 grid(8 * ((bhn + 7) / 8) * ((cap + kUnitBundle - 1) / kUnitBundle)), block(64 * kUnitBundle);
+  const dim3 grid(8 * ((bhn + 7) / 8) * ((a.nq + kUnitBundle - 1) / kUnitBundle)), block(64 * kUnitBundle);
   hipLaunchKernelGGL((attn_rows_kernel<D>), grid, block, 0, stream, a);
 }
 

@@ -58,9 +58,14 @@ size_t support_workspace_bytes(int bh, int nq);
 __host__ __device__ constexpr int mass_ws_slot(int block) { return block == 16 ? 64 : 32; }
 size_t mass_ws_bytes(int64_t bh, int nq, int block);
 // The schedule's work units for the bf16 sparse kernel (wise_build_support's
-// plan): per head a count, then unit_slots(nq) slots of units
-// (query block << 8) | (part << 4) | (parts - 1) or -1, run kUnitBundle to a
-// workgroup; a row splits in at most kUnitBundle parts, all in one bundle.
+// plan): per head a count, then unit_slots(nq) slots of kUnitInts ints each:
+// (query block << 8) | (part << 4) | (parts - 1) or -1, the unit's first and
+// one-past-last CSR entry, and its first key block (-1 if none); run
+// kUnitBundle to a workgroup; a row splits in at most kUnitBundle parts, all
+// in one bundle.
+constexpr int kUnitInts = 4;
+// the unit slots start after the counts, at a multiple of 4 ints (16 bytes)
+__host__ __device__ constexpr int unit_base(int bh) { return (bh + 3) & ~3; }
 constexpr int kUnitBundle = 4;
 __host__ __device__ constexpr int unit_slots(int nq) { return 4 * nq; }
 // resident row wavefronts of the sparse kernel per CU (two per SIMD)

@@ -340,7 +340,8 @@ static_assert(kMaxNq <= 4096 && kUnitBundle == 4, "unit sort key: class, 13-bit 
 __device__ __forceinline__ int unit_parts(int n, int len) { return n <= len ? 1 : (n <= 2 * len ? 2 : 4); }
 
 __global__ __launch_bounds__(kOrderThreads) void make_units_kernel(const int32_t* counts, int nq, int bh,
-                                                                   const int32_t* nnz, int row_slots,
+                                                                   const int32_t* nnz, const int32_t* row_ptr,
+                                                                   const int32_t* col_idx, int row_slots,
                                                                    int32_t* plan) {
   extern __shared__ uint32_t keys[];  // unit_slots(nq) keys
   __shared__ int32_t part_sum[kOrderThreads / 64];
@@ -404,23 +405,29 @@ __global__ __launch_bounds__(kOrderThreads) void make_units_kernel(const int32_t
     }
   // sorted order = slot order: 4-part rows fill whole bundles (their count is a
   // multiple of 4), 2-part rows start at even slots; plan[h] = the head's unit
-  // count, its units at plan[bh + h * unit_slots(nq) ..]:
-  // (query block << 8) | (part << 4) | (parts - 1), -1 past the count
+  // count, its units at plan[unit_base(bh) + (h * unit_slots(nq) + x) * kUnitInts]:
+  // (query block << 8) | (part << 4) | (parts - 1), the part's CSR entries
+  // [e0, e1), its first key block (all -1 past the count)
   if (tid == 0) plan[h] = units;
-  int32_t* out = plan + bh + (size_t)h * cap;
+  if (h == 0 && tid < unit_base(bh) - bh) plan[bh + tid] = -1;  // the padding after the counts
+  int32_t* out = plan + unit_base(bh) + (size_t)h * cap * kUnitInts;
   for (int x = tid; x < cap; x += kOrderThreads) {
+    int4 e = make_int4(-1, -1, -1, -1);
     if (x < units) {
       const uint32_t key = keys[x];
       const int r = (int)((key >> 2) & 0xFFFu), p = (int)(key & 3u);
-      const int parts = unit_parts(min(max(cnt[r], 0), nq), len);
-      out[x] = (r << 8) | (p << 4) | (parts - 1);
-    } else {
-      out[x] = -1;
+      const int n = min(max(cnt[r], 0), nq), parts = unit_parts(n, len);
+      const int row0 = row_ptr[(size_t)h * nq + r];
+      e.x = (r << 8) | (p << 4) | (parts - 1);
+      e.y = row0 + (int)((int64_t)n * p / parts);
+      e.z = row0 + (int)((int64_t)n * (p + 1) / parts);
+      e.w = e.z > e.y ? col_idx[e.y] : -1;
     }
+    reinterpret_cast<int4*>(out)[x] = e;
   }
 }
 
-size_t plan_capacity(int bh, int nq) { return (size_t)bh + (size_t)bh * unit_slots(nq); }
+size_t plan_capacity(int bh, int nq) { return (size_t)unit_base(bh) + (size_t)bh * unit_slots(nq) * kUnitInts; }
 
 size_t support_workspace_bytes(int bh, int nq) {
   const size_t rows = (size_t)bh * nq;
@@ -484,7 +491,7 @@ static hipError_t finish_schedule(int bh, int nq, int32_t* row_ptr, int32_t* col
   e = hipGetLastError();
   if (e != hipSuccess || plan == nullptr) return e;
   hipLaunchKernelGGL(make_units_kernel, dim3(bh), dim3(kOrderThreads), (size_t)unit_slots(nq) * sizeof(uint32_t),
-                     stream, counts, nq, bh, nnz, row_slots, plan);
+                     stream, counts, nq, bh, nnz, row_ptr, col_idx, row_slots, plan);
   return hipGetLastError();
 }
 

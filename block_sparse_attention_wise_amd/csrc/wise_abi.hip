@@ -88,7 +88,7 @@ wise_status check_build(int bh, int nq, int num_steps, const float* mass, int32_
   if (workspace_bytes < (workspace_need ? workspace_need : support_workspace_bytes(bh, nq))) return WISE_ERR_INVALID_ARG;
   if (plan != nullptr) {
     const size_t need = wise_build_support_plan_capacity(bh, nq);
-    if (need == 0 || !aligned4(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
+    if (need == 0 || !aligned16(plan) || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
   }
   return WISE_OK;
 }
@@ -293,7 +293,7 @@ wise_status wise_sparse_attn(wise_dtype dt, int batch, int heads, int kv_heads, 
     // every unit slot of every head must be readable
     const int64_t bh = (int64_t)batch * heads;
     const size_t need = bh <= INT32_MAX ? wise_build_support_plan_capacity((int)bh, seqlen / kBlock) : 0;
-    if (!aligned4(plan) || need == 0 || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
+    if (!aligned16(plan) || need == 0 || plan_capacity < (int64_t)need) return WISE_ERR_INVALID_ARG;
     // the fp32 kernel and 16-token schedules walk the CSR rows
     if (dt != WISE_BF16 || block != kBlock) plan = nullptr;
   }

@@ -117,8 +117,9 @@ size_t wise_build_support_workspace_bytes(int bh, int nq, int num_steps);
 
 /*
  * int32 entries of the optional work-unit list wise_build_support can emit
- * beside the CSR schedule for bh rows of nq query blocks: bh + bh * 4 * nq
- * (0 on invalid sizes).
+ * beside the CSR schedule for bh rows of nq query blocks:
+ * B + bh * 4 * nq * 4 with B = bh rounded up to a multiple of 4 (0 on invalid
+ * sizes).
  */
 size_t wise_build_support_plan_capacity(int bh, int nq);
 
@@ -153,13 +154,18 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 resident row wavefronts of the current device (8 per CU) and
  *                 n_head the head's scheduled blocks: P = 2 for n <= 2L, else 4.
  *                 The kernel runs units four to a workgroup, a split row's
- *                 parts in one.  plan[h] (h < bh) is head h's unit count U_h,
- *                 and plan[bh + h*4*nq + j] for j < U_h its units,
- *                 (query block << 8) | (part << 4) | (P - 1), in the order: the
- *                 units of 4-part rows, then of 2-part rows, then whole rows,
- *                 each class by ceil(n / P) descending, then query block, then
- *                 part (so a 4-part row fills slots 4k .. 4k+3 and a 2-part row
- *                 starts at an even slot); -1 for j >= U_h.
+ *                 parts in one.  plan[h] (h < bh) is head h's unit count U_h
+ *                 (plan[bh .. B-1] = -1);
+ *                 unit j < U_h of head h is the four int32 at
+ *                 plan + B + 4*(h*4*nq + j) (B = bh rounded up to a multiple of
+ *                 4): (query block << 8) | (part << 4) | (P - 1), the first and
+ *                 one-past-last index of its CSR entries in col_idx, and its
+ *                 first key block (col_idx at the first index; -1 if it has no
+ *                 entry).  Units come in the order: those of 4-part rows, then
+ *                 of 2-part rows, then whole rows, each class by ceil(n / P)
+ *                 descending, then query block, then part (so a 4-part row
+ *                 fills slots 4k .. 4k+3 and a 2-part row starts at an even
+ *                 slot); all four values are -1 for j >= U_h.
  *   workspace   : device scratch of at least
  *                 wise_build_support_workspace_bytes(bh, nq, num_steps) bytes;
  *                 its contents on entry do not matter.
@@ -281,7 +287,8 @@ wise_status wise_retained_mass(int bh, int nq, const float* mass, const int32_t*
  *                            for this same schedule, plan_capacity its readable
  *                            int32 entries (at least
  *                            wise_build_support_plan_capacity(batch*heads,
- *                            seqlen / 32), else WISE_ERR_INVALID_ARG).  The bf16
+ *                            seqlen / 32), and plan 16-byte aligned, else
+ *                            WISE_ERR_INVALID_ARG).  The bf16
  *                            kernel at block 32 gives every unit (without units:
  *                            every query block's row) one wavefront of its own,
  *                            which walks the unit's CSR entries, four units to a

@@ -141,9 +141,9 @@ def test_workspace_bytes(lib):
 def test_plan_capacity(lib):
     f = lib.wise_build_support_plan_capacity
     assert f(0, 8) == 0 and f(1, 0) == 0 and f(1, 4097) == 0
-    # a unit count per head, then 4 nq unit slots per head
+    # a unit count per head (padded to 4), then 4 nq unit slots of 4 ints per head
     for bh, nq in ((1, 8), (32, 128), (3, 33), (1, 1)):
-        assert f(bh, nq) == bh + bh * 4 * nq
+        assert f(bh, nq) == (bh + 3) // 4 * 4 + bh * 4 * nq * 4
 
 
 def _build(lib, bh=2, nq=8, steps=4, mass=P, eta=0.95, rp=P, ci=P, cap=None, nnz=P, plan=NULL, pcap=0,
@@ -166,7 +166,7 @@ def test_build_support_validation(lib):
     assert _build(lib, wsb=16) == INVALID
     need = lib.wise_build_support_plan_capacity(2, 8)
     assert _build(lib, plan=P, pcap=need - 1) == INVALID
-    assert _build(lib, plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
+    assert _build(lib, plan=ctypes.c_void_p(0x10008), pcap=need) == INVALID
     # a worst case beyond int32 row offsets is rejected
     assert _build(lib, bh=1 << 20, nq=4096, cap=1 << 62, wsb=1 << 62) == INVALID
 
@@ -192,10 +192,10 @@ def test_sparse_validation(lib):
     assert sp(q=MIS) == INVALID
     assert sp(hk=2) == INVALID                          # more kv heads than query heads
     assert sp(d=80) == UNSUPPORTED
-    need = lib.wise_build_support_plan_capacity(1, 4)    # a count and 16 unit slots
-    assert need == 1 + 16
+    need = lib.wise_build_support_plan_capacity(1, 4)    # a count (padded to 4) and 16 unit slots of 4 ints
+    assert need == 4 + 16 * 4
     assert sp(plan=P, pcap=need - 1) == INVALID         # a unit slot would be out of reach
-    assert sp(plan=ctypes.c_void_p(0x10002), pcap=need) == INVALID
+    assert sp(plan=ctypes.c_void_p(0x10008), pcap=need) == INVALID   # unit slots are 16-byte records
 
 
 def test_variant_and_retained_validation(lib):

@@ -362,12 +362,13 @@ def test_uniform_attention_closed_form_on_gpu():
     assert_mass_close(f64(mass[0]), O.block_mass(np.zeros((n, d)), f64(k[0, 0])), "bf16", "uniform mass")
 
 
-def _expected_units(counts, nq, nnz, slots):
+def _expected_units(counts, nq, nnz, slots, row_ptr_h, col_idx):
     """The work units of wise_build_support, on the host, for one head: unit
     length L = max(4, ceil(nnz / slots), ceil(head blocks / nq)); a row of n > L
     blocks splits in P = 2 parts (n <= 2 L) or 4; units of 4-part rows, then
     2-part rows, then whole rows, each by ceil(n / P) descending, then row, then
-    part; encoded (row << 8) | (part << 4) | (P - 1)."""
+    part; each as (row << 8) | (part << 4) | (P - 1), the part's CSR entries
+    [e0, e1) (part p of n entries: n p / P .. n (p + 1) / P) and its first block."""
     length = max(4, -(-nnz // slots), -(-sum(counts) // nq))
     units = []
     for r, n in enumerate(counts):
@@ -376,7 +377,12 @@ def _expected_units(counts, nq, nnz, slots):
         cls = {4: 0, 2: 1, 1: 2}[parts]
         units += [(cls, -ul, r, p, parts) for p in range(parts)]
     units.sort()
-    return [(r << 8) | (p << 4) | (parts - 1) for _, _, r, p, parts in units]
+    out = []
+    for _, _, r, p, parts in units:
+        n = counts[r]
+        e0, e1 = row_ptr_h[r] + n * p // parts, row_ptr_h[r] + n * (p + 1) // parts
+        out.append([(r << 8) | (p << 4) | (parts - 1), e0, e1, int(col_idx[e0]) if e1 > e0 else -1])
+    return out
 
 
 @pytest.mark.parametrize("bh,nq,eta", [(3, 37, 0.9), (2, 8, 0.5), (1, 130, 0.95), (2, 5, 1.0), (1, 300, 0.99),
@@ -397,8 +403,11 @@ def test_work_units_split_long_rows(bh, nq, eta):
     note(f"work units bh={bh} nq={nq} eta={eta}")
     sched = wise.build_support(torch.from_numpy(m).to(DEV), eta)
     torch.cuda.synchronize()
-    assert sched.plan is not None and sched.plan.numel() == bh + bh * 4 * nq
+    base = (bh + 3) // 4 * 4
+    assert sched.plan is not None and sched.plan.numel() == base + bh * 4 * nq * 4
     plan = sched.plan.cpu().numpy()
+    rp_host = sched.row_ptr.cpu().numpy()
+    ci_host = sched.col_idx.cpu().numpy()
     gpu_rows = csr_rows(sched.row_ptr, sched.col_idx)
     ref_rows, flags = [], []
     for r in range(bh):
@@ -413,12 +422,12 @@ def test_work_units_split_long_rows(bh, nq, eta):
     split = 0
     for h in range(bh):
         counts = [len(gpu_rows[h * nq + q]) for q in range(nq)]
-        want = _expected_units(counts, nq, nnz, slots)
-        got = plan[bh + h * 4 * nq:bh + (h + 1) * 4 * nq]
+        want = _expected_units(counts, nq, nnz, slots, rp_host[h * nq:(h + 1) * nq], ci_host)
+        got = plan[base + h * 4 * nq * 4:base + (h + 1) * 4 * nq * 4].reshape(4 * nq, 4)
         assert int(plan[h]) == len(want) <= 4 * nq, f"head {h}: unit count"
         assert got[:len(want)].tolist() == want, f"head {h}: units"
         assert np.all(got[len(want):] == -1)
-        split += sum(1 for u in want if (u & 15) > 0)
+        split += sum(1 for u in want if (u[0] & 15) > 0)
     # cover the split path: a schedule whose units include split rows ...
     n, d = 32 * nq, 128
     if nq > 300:
@@ -432,11 +441,19 @@ def test_work_units_split_long_rows(bh, nq, eta):
     # ... and the same schedule with every row forced into 4 parts (hand-made units,
     # one workgroup per row; rows with fewer than 4 blocks leave parts empty:
     # log-sum-exp -inf, weight 0)
-    forced = np.full(bh + bh * 4 * nq, -1, dtype=np.int32)
+    forced = np.full(base + bh * 4 * nq * 4, -1, dtype=np.int32)
     for h in range(bh):
         forced[h] = 4 * nq
-        forced[bh + h * 4 * nq:bh + (h + 1) * 4 * nq] = [(qb << 8) | (p << 4) | 3 for qb in range(nq)
-                                                        for p in range(4)]
+        us = []
+        for qb in range(nq):
+            r0, n_ = int(rp_host[h * nq + qb]), int(rp_host[h * nq + qb + 1] - rp_host[h * nq + qb])
+            for p in range(4):
+                e0, e1 = r0 + n_ * p // 4, r0 + n_ * (p + 1) // 4
+                # the first block as the builder writes it (parts 0, 3), left out (part 1: the
+                # kernel finds it from the CSR) or wrong (part 2: the kernel drops that copy)
+                fb = int(ci_host[e0]) if e1 > e0 else -1
+                us.append([(qb << 8) | (p << 4) | 3, e0, e1, {1: -1, 2: qb}.get(p, fb)])
+        forced[base + h * 4 * nq * 4:base + (h + 1) * 4 * nq * 4] = np.array(us, dtype=np.int32).ravel()
     rows_forced = set(range(nq))
     fsched = wise.Schedule(sched.row_ptr, sched.col_idx, sched.nnz, bh, nq, plan=torch.from_numpy(forced).to(DEV))
     of, lf = wise.sparse_attn(dq, dk, dv, fsched, want_lse=True)
