@@ -60,6 +60,7 @@ struct SupportArgs {
   const int32_t* ref_row_ptr;  // matched kinds: the reference schedule
   const int32_t* ref_col_idx;
   int64_t ref_cap;
+  int wstride;  // keys per wavefront of the per-step path (0: the workgroup path only)
 };
 
 __device__ __forceinline__ double block_exclusive_scan(double x, double* wsum, int tid) {
@@ -84,6 +85,17 @@ __device__ __forceinline__ double block_exclusive_scan(double x, double* wsum, i
 // quarter of the key buffer, synchronising only within the wavefront.
 constexpr int kWaveSortMax = kMaxNq / (kSelThreads / 64);
 
+// The key buffer (dynamic LDS) is sized for the launch's longest row: the sorts
+// are bound by LDS round trips and wavefront syncs, so a smaller buffer buys
+// more resident workgroups.  Sets a.wstride and returns the buffer's bytes.
+static size_t select_lds_bytes(SupportArgs& a) {
+  int n2 = 1;
+  while (n2 < a.nq) n2 <<= 1;
+  a.wstride = a.kind == kCumulative ? (n2 < kWaveSortMax ? n2 : kWaveSortMax) : 0;
+  const int nkeys = n2 > 4 * a.wstride ? n2 : 4 * a.wstride;
+  return (size_t)nkeys * sizeof(uint64_t);
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -91,7 +103,8 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a) {
-  __shared__ uint64_t keys[kMaxNq];
+  extern __shared__ uint64_t sel_keys[];  // max(n2, 4 * wstride) keys
+  uint64_t* const keys = sel_keys;
   __shared__ uint32_t uni[kMaxNq / 32];
   __shared__ uint32_t refm[kMaxNq / 32];
   __shared__ double wsum[kSelThreads / 64];
@@ -122,10 +135,10 @@ __global__ __launch_bounds__(kSelThreads) void select_union_kernel(SupportArgs a
     for (int w = 0; w < a.nwords; ++w) ref_count += __popc(refm[w]);
   }
 
-  if (a.kind == kCumulative && n2 <= kWaveSortMax) {
+  if (a.kind == kCumulative && n2 <= a.wstride) {
     __syncthreads();  // uni cleared
     const int wave = tid >> 6, lane = tid & 63;
-    uint64_t* kw = keys + wave * kWaveSortMax;
+    uint64_t* kw = keys + wave * a.wstride;
     for (int t = wave; t < a.steps; t += kSelThreads / 64) {
       const float* mrow = a.mass + (((size_t)t * a.bh + bh) * a.nq + qb) * (size_t)a.nq;
       for (int e = lane; e < n2; e += 64)
@@ -515,7 +528,8 @@ hipError_t launch_support(const float* mass, int bh, int nq, int steps, double e
   a.ref_row_ptr = ref_row_ptr;
   a.ref_col_idx = ref_col_idx;
   a.ref_cap = ref_cap;
-  hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, a);
+  const size_t lds = select_lds_bytes(a);
+  hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)rows), dim3(kSelThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return finish_schedule(bh, nq, row_ptr, col_idx, nnz, plan, row_slots, workspace, stream);
@@ -606,7 +620,8 @@ hipError_t launch_support_blocked(const float* mass, int bh, int nq, int steps, 
   a.ref_row_ptr = nullptr;
   a.ref_col_idx = nullptr;
   a.ref_cap = 0;
-  hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)((size_t)bh * nqb)), dim3(kSelThreads), 0, stream, a);
+  const size_t lds = select_lds_bytes(a);
+  hipLaunchKernelGGL(select_union_kernel, dim3((unsigned)((size_t)bh * nqb)), dim3(kSelThreads), lds, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t rows = (size_t)bh * nq;
