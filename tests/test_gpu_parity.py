@@ -522,3 +522,67 @@ def test_high_dynamic_range_logits():
         worst = [max(worst[0], ea, es), max(worst[1], er, rs)]
     record("high dynamic range (logit span > 60, dominant key)", rows=heads * nq, max_abs=worst[0],
            tol_used=worst[1])
+
+
+def test_maximum_context_schedule_units_and_sparse_rows():
+    """The longest context the bf16 path takes: 4096 query blocks (n = 131072, one
+    head, d = 64), masses fed for two discovery steps.  Sampled rows on both of
+    the selection kernel's paths (rows of up to 1024 blocks sorted by one
+    wavefront per step, longer rows by the whole workgroup, keys up to 4096 per
+    row) match the oracle outside boundary-flagged blocks; the work units follow
+    the host rule (4 nq unit slots, the unit sort's largest LDS buffer); sparse
+    attention of sampled query blocks, through the units, matches the oracle
+    over the GPU's own rows."""
+    wise = _wise()
+    nq, d, steps, eta = 4096, 64, 2, 0.9
+    n = 32 * nq
+    rng = np.random.default_rng(131072)
+    m = np.zeros((steps, 1, nq, nq), dtype=np.float32)
+    for s in range(steps):
+        g = np.tril(rng.gamma(0.4, size=(nq, nq)))  # Dirichlet(0.4) rows over blocks 0..q
+        m[s, 0] = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+        del g
+    note(f"maximum context: build nq={nq}")
+    sched = wise.build_support(torch.from_numpy(m).to(DEV), eta)
+    torch.cuda.synchronize()
+    rp_host = sched.row_ptr.cpu().numpy()
+    ci_host = sched.col_idx.cpu().numpy()
+    nnz = int(sched.nnz.item())
+    assert nnz == int(rp_host[-1])
+    gpu_rows = [np.sort(ci_host[rp_host[r]:rp_host[r + 1]]) for r in range(nq)]
+    sample = [0, 1, 511, 1022, 1023, 1024, 1025, 2047, 2048, 3001, 4094, 4095]
+    flagged_rows = 0
+    for qb in sample:
+        sup, flags = oracle_union_row([m[s, 0, qb, :qb + 1].astype(np.float64) for s in range(steps)], eta)
+        diff = set(gpu_rows[qb].tolist()) ^ set(sup.tolist())
+        assert diff <= flags, f"row {qb}: unflagged mismatch {sorted(diff - flags)[:8]}"
+        flagged_rows += int(bool(diff))
+    assert flagged_rows <= flagged_row_bound(len(sample))
+    # work units: the host rule over the GPU's own rows
+    base = 4
+    plan = sched.plan.cpu().numpy()
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * 8
+    want = _expected_units([len(r) for r in gpu_rows], nq, nnz, slots, rp_host[:nq], ci_host)
+    got = plan[base:base + 4 * nq * 4].reshape(4 * nq, 4)
+    assert int(plan[0]) == len(want) <= 4 * nq
+    assert got[:len(want)].tolist() == want
+    assert np.all(got[len(want):] == -1)
+    # sparse attention through the units, sampled query blocks against the oracle
+    tg = torch.Generator().manual_seed(4096)
+    q, k, v = (torch.randn((1, 1, n, d), generator=tg).to(torch.bfloat16) for _ in range(3))
+    note(f"maximum context: sparse attention n={n}")
+    o, lse = wise.sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), sched, want_lse=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
+    worst_abs = worst_tol = 0.0
+    for qb in sample:
+        rows = [np.array([0])] * nq
+        rows[qb] = gpu_rows[qb]
+        ro, rl = O.sparse_attention(qh, kh, vh, rows, qblocks=(qb, qb + 1))
+        sl = slice(32 * qb, 32 * qb + 32)
+        ea, er = assert_attn_close(f64(o[0, 0, sl]), ro, "bf16", f"maximum context block {qb} O")
+        assert_lse_close(f64(lse[0, 0, sl]), rl, "bf16", f"maximum context block {qb}")
+        worst_abs, worst_tol = max(worst_abs, ea), max(worst_tol, er)
+    split = sum(1 for u in want if (u[0] & 15) > 0)
+    record(f"maximum context nq={nq} (n {n}, eta {eta}, {steps} steps)", rows=len(sample), nnz=nnz,
+           split_parts=split, flagged_rows=flagged_rows, max_abs=worst_abs, tol_used=worst_tol)
