@@ -950,10 +950,11 @@ __global__ __launch_bounds__(64 * kSparseWaves) __attribute__((
 // through one LDS slot of its own, with no barrier: at the start of a step the
 // block's K and V operands move from the slot to registers, the slot refills
 // with the next block, and the block is computed from the registers while that
-// copy runs.  Two wavefronts share each SIMD, so one's copy waits, set-up and
-// output stores overlap the other's matrix work.  A workgroup runs a bundle of
-// kUnitBundle units; a split row's parts share a bundle and merge through LDS
-// after the bundle's one barrier: with L_p the parts' log-sum-exps (log2 units)
+// copy runs.  Two wavefronts (four at d = 64) share each SIMD, so one's copy
+// waits, set-up and output stores overlap another's matrix work.  A workgroup
+// runs a bundle of kUnitBundle units; a split row's parts share a bundle and
+// merge through LDS after the bundle's one barrier: with L_p the parts'
+// log-sum-exps (log2 units)
 // and O_p their normalised outputs, L = log2 sum_p 2^L_p and
 // O = sum_p 2^(L_p - L) O_p.
 //
@@ -968,10 +969,17 @@ constexpr int rows_lds_bytes() {
 }
 // Row-stream wavefronts resident per CU: two per SIMD, whole bundles within the
 // 160 KiB of LDS.
+// Wavefronts per SIMD of the row-stream kernel: four at d = 64 (128 VGPRs,
+// 8 KiB slots: sixteen wavefronts per CU), else two (three at d = 96 measured
+// 9% slower on the 220-head step).
+template <int D>
+constexpr int rows_occupancy() {
+  return D == 64 ? 4 : 2;
+}
 template <int D>
 constexpr int rows_per_cu() {
   constexpr int by_lds = (160 * 1024) / (kUnitBundle * rows_lds_bytes<D>()) * kUnitBundle;
-  return by_lds < kRowWavesPerCu ? by_lds : kRowWavesPerCu;
+  return by_lds < 4 * rows_occupancy<D>() ? by_lds : 4 * rows_occupancy<D>();
 }
 
 // Ascending walk over the set bits of a row bitmask of nw words.
@@ -1003,7 +1011,8 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int D>
-__global__ __launch_bounds__(64 * kUnitBundle) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_rows_kernel(
+__global__ __launch_bounds__(64 * kUnitBundle) __attribute__((
+    amdgpu_waves_per_eu(rows_occupancy<D>(), rows_occupancy<D>()))) void attn_rows_kernel(
     AttnBf16Args a) {
   using T = Tile<D>;
   constexpr int CI = D / 16;  // wave-copies per tile
