@@ -338,8 +338,11 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
 // n p / P .. n (p+1) / P - 1 of its n) when the row is longer than the unit
 // length L: P = 2 for n <= 2 L, else 4.  L is the schedule's scheduled blocks
 // per resident row wavefront of the GPU (row_slots), so that no unit outlasts
-// the average slot's work, and at least the head's mean row length and
-// kUnitMin blocks.  A split row's parts share a bundle, which merges them from
+// the average slot's work, but at most kUnitMeanCap times the head's mean row
+// length m (where the GPU has far more rows than slots, as at 16k contexts,
+// shorter units balance better), and at least m and kUnitMin blocks:
+// L = max(kUnitMin, m, min(ceil(nnz / row_slots), kUnitMeanCap m)).  A split
+// row's parts share a bundle, which merges them from
 // LDS at its end.  A head's slots list the units of 4-part rows first (a bundle
 // each), then those of 2-part rows (two rows per bundle), then whole rows, each
 // class by unit length descending (ties: lower query block, then lower part):
@@ -348,6 +351,7 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
 // floating-point sums.
 constexpr int kOrderThreads = 256;
 constexpr int kUnitMin = 4;
+constexpr int kUnitMeanCap = 3;
 static_assert(kMaxNq <= 4096 && kUnitBundle == 4, "unit sort key: class, 13-bit length, 12-bit row, 2-bit part");
 
 __device__ __forceinline__ int unit_parts(int n, int len) { return n <= len ? 1 : (n <= 2 * len ? 2 : 4); }
@@ -374,7 +378,8 @@ __global__ __launch_bounds__(kOrderThreads) void make_units_kernel(const int32_t
   for (int k = 0; k < kOrderThreads / 64; ++k) head_total += part_sum[k];
   const int64_t total = max(*nnz, 0);
   const int slots = max(row_slots, 1);
-  const int len = max(max(kUnitMin, (int)((total + slots - 1) / slots)), (head_total + nq - 1) / nq);
+  const int mean = (head_total + nq - 1) / nq;
+  const int len = max(max(kUnitMin, mean), min((int)((total + slots - 1) / slots), kUnitMeanCap * mean));
   // this thread's units, then an exclusive scan over the threads
   int mine = 0;
   for (int r = r0; r < r1; ++r) mine += unit_parts(min(max(cnt[r], 0), nq), len);

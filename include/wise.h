@@ -57,7 +57,7 @@ typedef enum {
   WISE_FP32 = 1  /* fp32 inputs/outputs, fp32 arithmetic throughout */
 } wise_dtype;
 
-#define WISE_ABI_VERSION 11
+#define WISE_ABI_VERSION 12
 
 int wise_abi_version(void);
 const char* wise_status_string(wise_status s);
@@ -150,9 +150,10 @@ size_t wise_build_support_plan_capacity(int bh, int nq);
  *                 A unit is one query block's row, or one of P near-equal
  *                 contiguous parts of its CSR entries (part p takes entries
  *                 n*p/P .. n*(p+1)/P - 1 of its n) when n exceeds the unit
- *                 length L = max(4, ceil(nnz / S), ceil(n_head / nq)), S the
+ *                 length L = max(4, m, min(ceil(nnz / S), 3 m)), S the
  *                 resident row wavefronts of the current device (8 per CU) and
- *                 n_head the head's scheduled blocks: P = 2 for n <= 2L, else 4.
+ *                 m = ceil(n_head / nq) the head's mean row length (n_head its
+ *                 scheduled blocks): P = 2 for n <= 2L, else 4.
  *                 The kernel runs units four to a workgroup, a split row's
  *                 parts in one.  plan[h] (h < bh) is head h's unit count U_h
  *                 (plan[bh .. B-1] = -1);

@@ -69,7 +69,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.wise_abi_version() == 11
+    assert lib.wise_abi_version() == 12
     for s in (OK, INVALID, UNSUPPORTED, HIPERR):
         assert lib.wise_status_string(s)
     assert lib.wise_status_string(99) == b"unknown status"

@@ -364,12 +364,14 @@ def test_uniform_attention_closed_form_on_gpu():
 
 def _expected_units(counts, nq, nnz, slots, row_ptr_h, col_idx):
     """The work units of wise_build_support, on the host, for one head: unit
-    length L = max(4, ceil(nnz / slots), ceil(head blocks / nq)); a row of n > L
+    length L = max(4, m, min(ceil(nnz / slots), 3 m)), m = ceil(head blocks / nq)
+    the head's mean row length; a row of n > L
     blocks splits in P = 2 parts (n <= 2 L) or 4; units of 4-part rows, then
     2-part rows, then whole rows, each by ceil(n / P) descending, then row, then
     part; each as (row << 8) | (part << 4) | (P - 1), the part's CSR entries
     [e0, e1) (part p of n entries: n p / P .. n (p + 1) / P) and its first block."""
-    length = max(4, -(-nnz // slots), -(-sum(counts) // nq))
+    mean = -(-sum(counts) // nq)
+    length = max(4, mean, min(-(-nnz // slots), 3 * mean))
     units = []
     for r, n in enumerate(counts):
         parts = 1 if n <= length else (2 if n <= 2 * length else 4)
