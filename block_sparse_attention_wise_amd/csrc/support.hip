@@ -24,8 +24,9 @@
 //                 nnz.
 //   emit_csr      one wavefront per row: expands the bitmask into ascending
 //                 col_idx entries at row_ptr[row].
-//   make_units    one workgroup per head: the head's work units for the sparse
-//                 kernel (rows, long rows split in parts), longest first.
+//   make_units    one 1024-thread workgroup per head: the head's work units for
+//                 the sparse kernel (rows, long rows split in parts), longest
+//                 first.
 #include "common.h"
 #include "kernels.h"
 
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(64) void emit_csr_kernel(const uint32_t* masks, int
 // the split classes' units are at most L long and the whole rows' at most L,
 // and within a class the longest start first.  Splitting only reorders
 // floating-point sums.
-constexpr int kOrderThreads = 256;
+constexpr int kOrderThreads = 1024;  // units of a head (up to 4 nq) sort in one workgroup
 constexpr int kUnitMin = 4;
 constexpr int kUnitMeanCap = 3;
 static_assert(kMaxNq <= 4096 && kUnitBundle == 4, "unit sort key: class, 13-bit length, 12-bit row, 2-bit part");
