@@ -9,7 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wise.h")
-LIB = os.path.join(ROOT, "block_sparse_attention_wise_amd", "libwise.so")
+# WISE_ABI_TEST_LIB: another build of the library to check (the host-sanitizer build)
+LIB = os.environ.get("WISE_ABI_TEST_LIB") or os.path.join(ROOT, "block_sparse_attention_wise_amd", "libwise.so")
 
 OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
 BF16, FP32 = 0, 1
