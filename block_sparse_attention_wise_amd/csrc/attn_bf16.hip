@@ -98,6 +98,22 @@ __device__ __forceinline__ void copy_to_lds(u32x4 rs, uint32_t lds, uint32_t vof
                : "m0");
 }
 
+// A unit record (4 ints at rec) and a count (at cnt) read through the scalar
+// data cache, which bypasses the vector memory pipeline the tile copies keep
+// busy; the wait sits in the same statement, so the registers are written
+// before the compiler sees them.  Read only: nothing writes through that cache.
+__device__ __forceinline__ void scalar_read_unit(const int* rec, const int* cnt, int4& ue, int& n) {
+  typedef int sx4 __attribute__((ext_vector_type(4)));
+  sx4 r;
+  int c;
+  asm volatile("s_load_dwordx4 %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(r), "=&s"(c)
+               : "s"(rec), "s"(cnt)
+               : "memory");
+  ue = make_int4(r[0], r[1], r[2], r[3]);
+  n = c;
+}
+
 // Key index (within a 32-key block) held by accumulator register r of a lane in
 // half h of the 32x32 MFMA result.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -1068,8 +1084,10 @@ __global__ __launch_bounds__(64 * kUnitBundle) __attribute__((
   if (a.plan != nullptr) {
     // this slot's unit (in bounds: s < cap) and the head's unit count load
     // together, and every field is decoded before the first branch
-    const int4 ue = reinterpret_cast<const int4*>(a.plan + unit_base(bhn))[(size_t)bh * cap + s];
-    const int units = min(a.plan[bh], cap);
+    int4 ue;
+    int count;
+    scalar_read_unit(a.plan + unit_base(bhn) + ((size_t)bh * cap + s) * kUnitInts, a.plan + bh, ue, count);
+    const int units = min(count, cap);
     const int u = s < units ? ue.x : -1;
     const int up = (u >> 4) & 15, un = (u & 15) + 1;
     // a part and its row's other parts lie in this bundle

@@ -588,3 +588,51 @@ def test_maximum_context_schedule_units_and_sparse_rows():
     split = sum(1 for u in want if (u[0] & 15) > 0)
     record(f"maximum context nq={nq} (n {n}, eta {eta}, {steps} steps)", rows=len(sample), nnz=nnz,
            split_parts=split, flagged_rows=flagged_rows, max_abs=worst_abs, tol_used=worst_tol)
+
+
+def test_sparse_repeated_launches_and_graph_replays():
+    """The bf16 sparse kernel with work units, launched back to back and replayed
+    from a captured graph (with other work between the replays), gives outputs
+    bit-identical to its first launch, and agrees with the CSR walk over the same
+    schedule."""
+    wise, w = _wise(), WORKLOADS["2k"]
+    g = _gen("2k")
+    mass = torch.empty((4, w.heads, w.nq, w.nq), dtype=torch.float32, device=DEV)
+    for si, t in enumerate((9, 10, 11, 12)):
+        q, k, v = g.step_torch(t, DEV)
+        wise.full_attn_mass(q, k, v, mass=mass[si])
+    sched = wise.build_support(mass, 0.95)
+    q, k, v = g.step_torch(13, DEV)
+    ref, ref_lse = wise.sparse_attn(q, k, v, sched, want_lse=True)
+    ref, ref_lse = ref.clone(), ref_lse.clone()
+    o = torch.empty_like(q)
+    lse = torch.empty_like(ref_lse)
+    for rep in range(3):
+        note(f"repeated sparse launch {rep}")
+        o.fill_(float("nan"))
+        wise.sparse_attn(q, k, v, sched, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref) and torch.equal(lse, ref_lse)
+    note("sparse graph capture")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            wise.sparse_attn(q, k, v, sched, out=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        note(f"sparse graph replay {rep}")
+        o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref) and torch.equal(lse, ref_lse)
+        wise.dense_attn(q, k, v)  # other work between the replays
+        torch.cuda.synchronize()
+    csr_only = wise.Schedule(sched.row_ptr, sched.col_idx, sched.nnz, w.heads, w.nq)
+    oc, lc = wise.sparse_attn(q, k, v, csr_only, want_lse=True)
+    torch.cuda.synchronize()
+    assert_attn_close(f64(ref), f64(oc), "bf16", "units vs CSR O")
+    assert float((ref_lse - lc).abs().max()) <= 1e-5
+    record("sparse repeated launches (2k, 3 launches, 3 graph replays)", rows=w.heads * w.nq)
