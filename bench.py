@@ -266,7 +266,8 @@ def support_diagnostics(wise, w, eta, steps, mass, sched, ws, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10, help="timed trajectories (balanced passes)")
+    ap.add_argument("--steps", type=int, default=200,
+                    help="timed trajectories (balanced passes; ~8 ms each at 4k, so ~1.7 s of timed GPU work)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="4k")
     ap.add_argument("--eta", type=float, default=None)
