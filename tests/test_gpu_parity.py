@@ -636,3 +636,53 @@ def test_sparse_repeated_launches_and_graph_replays():
     assert_attn_close(f64(ref), f64(oc), "bf16", "units vs CSR O")
     assert float((ref_lse - lc).abs().max()) <= 1e-5
     record("sparse repeated launches (2k, 3 launches, 3 graph replays)", rows=w.heads * w.nq)
+
+
+@pytest.mark.parametrize("name", ["2k", "huginn4k"])
+def test_sparse_bundle_order_does_not_change_results(name):
+    """Order independence of the work-unit sparse kernel: the builder's units,
+    with the bundles of every head reversed, and shuffled, run the same units on
+    other workgroups in another order (a permuted grid), and must give outputs
+    and log-sum-exps bit-identical to the builder's order.  Every output row is
+    written by one wavefront (a split row merged inside its bundle in a fixed
+    order), so nothing may depend on which workgroup runs it or when."""
+    wise, w = _wise(), WORKLOADS[name]
+    g = _gen(name)
+    bh, nq = w.batch * w.heads, w.nq
+    mass = torch.empty((4, bh, nq, nq), dtype=torch.float32, device=DEV)
+    for si, t in enumerate((9, 10, 11, 12)):
+        q, k, v = g.step_torch(t, DEV)
+        wise.full_attn_mass(q, k, v, mass=mass[si])
+    sched = wise.build_support(mass, w.etas[0])
+    q, k, v = g.step_torch(17, DEV)
+    ref, ref_lse = wise.sparse_attn(q, k, v, sched, want_lse=True)
+    torch.cuda.synchronize()
+    plan = sched.plan.cpu().numpy()
+    base = (bh + 3) // 4 * 4
+    cap = 4 * nq
+    rng = np.random.default_rng(7)
+    split_bundles = 0
+    for order in ("reversed", "shuffled"):
+        perm = plan.copy()
+        for h in range(bh):
+            units = int(plan[h])
+            nb = (units + 3) // 4
+            slots = plan[base + h * cap * 4:base + (h + 1) * cap * 4].reshape(cap, 4)
+            bundles = slots[:4 * nb].reshape(nb, 4, 4)
+            split_bundles += int(np.sum(np.any((bundles[:, :, 0] >= 0) & ((bundles[:, :, 0] & 15) > 0), axis=1)))
+            idx = np.arange(nb)[::-1] if order == "reversed" else rng.permutation(nb)
+            out = np.full((cap, 4), -1, dtype=np.int32)
+            out[:4 * nb] = bundles[idx].reshape(4 * nb, 4)
+            # the count covers every slot of the last bundle: unused slots hold -1 units
+            perm[h] = 4 * nb
+            perm[base + h * cap * 4:base + (h + 1) * cap * 4] = out.ravel()
+        note(f"bundle order {order} ({name})")
+        psched = wise.Schedule(sched.row_ptr, sched.col_idx, sched.nnz, bh, nq, plan=torch.from_numpy(perm).to(DEV))
+        o = torch.full_like(ref, float("nan"))
+        lse = torch.full_like(ref_lse, float("nan"))
+        wise.sparse_attn(q, k, v, psched, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), f"{order}: outputs differ"
+        assert torch.equal(lse, ref_lse), f"{order}: log-sum-exps differ"
+    assert split_bundles > 0  # the permutation moved split rows too
+    record(f"sparse bundle order ({name}: reversed, shuffled)", rows=bh * nq, split_bundles=split_bundles // 2)
